@@ -1,0 +1,194 @@
+"""ctypes wrapper of the plain CPU oracle (tks_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.  It
+shares no code with the GPU path; only the seeded input generator
+(``tks_inputs``) feeds both.
+
+All functions take numpy arrays in the path's storage formats (bf16 bit
+patterns as uint16, e4m3fn codes as uint8) and return numpy arrays; scores
+come back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tks_oracle.c")
+_LIB = os.path.join(_HERE, "libtks_oracle.so")
+
+FORCE_FIRST = 1
+FORCE_LOCAL = 2
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "n_q", "n_k", "heads", "dim", "q_pos0", "causal_ratio", "key_fp8")]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, u32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+        SP = ctypes.POINTER(_Shape)
+        L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_double.restype = ctypes.c_double
+        L.orc_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3fn_to_double.restype = ctypes.c_double
+        L.orc_double_to_bf16.argtypes = [ctypes.c_double]
+        L.orc_double_to_bf16.restype = ctypes.c_uint16
+        L.orc_n_visible.argtypes = [SP, i64]
+        L.orc_n_visible.restype = i64
+        L.orc_index_scores.argtypes = [SP, P, P, P, P, i32, i32, i32, i32, P]
+        L.orc_topk_flat.argtypes = [SP, P, P, P, P, i32, P, i64, P, P]
+        L.orc_pool.argtypes = [SP, P, P, i32, P]
+        L.orc_block_select.argtypes = [SP, P, P, P, i32, i32, u32, P, i64, i32, P, P]
+        L.orc_refine.argtypes = [SP, P, P, P, P, i32, P, i32, i32, P, i64, P, P]
+        L.orc_hisa.argtypes = [SP, P, P, P, P, i32, i32, u32, i32, P, i64, P, P, P]
+        L.orc_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _shape(batch, n_q, n_k, heads, dim, q_pos0=0, causal_ratio=1, key_dtype=0):
+    return _Shape(batch, n_q, n_k, heads, dim, q_pos0, causal_ratio, int(key_dtype))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return None if a is None else np.ascontiguousarray(a, dtype=dt)
+
+
+def _keys(k, key_dtype):
+    return _c(k, np.uint8 if key_dtype else np.uint16)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments (rc=%d)" % (what, rc))
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().orc_bf16_to_double(int(bits))
+
+
+def e4m3fn_to_double(code: int) -> float:
+    return lib().orc_e4m3fn_to_double(int(code))
+
+
+def double_to_bf16(x: float) -> int:
+    return int(lib().orc_double_to_bf16(float(x)))
+
+
+def n_visible(shape: dict, t: int) -> int:
+    S = _shape(**shape)
+    return int(lib().orc_n_visible(ctypes.byref(S), int(t)))
+
+
+def index_scores(shape: dict, q, w, k, k_scale, q_begin, q_count, k_begin, k_count):
+    """[batch, q_count, k_count] float64 scores (-inf where not visible).
+    q / w: the full [batch, n_q, ...] arrays."""
+    S = _shape(**shape)
+    q, w, k, ks = _c(q, np.uint16), _c(w, np.float32), _keys(k, S.key_fp8), _c(k_scale, np.float32)
+    out = np.empty((S.batch, q_count, k_count), np.float64)
+    _check(lib().orc_index_scores(ctypes.byref(S), _ptr(q), _ptr(w), _ptr(k), _ptr(ks),
+                                  q_begin, q_count, k_begin, k_count, _ptr(out)), "index_scores")
+    return out
+
+
+def topk_flat(shape: dict, q_rows, w_rows, k, k_scale, topk, rows, with_vals=True):
+    """Flat top-k of the listed flat rows (b*n_q+t).  q_rows: [n, H, D] bf16 bits,
+    w_rows: [n, H].  Returns (idx int32 [n, topk], vals float64 [n, topk] or None)."""
+    S = _shape(**shape)
+    rows = _c(rows, np.int64)
+    q, w, k, ks = _c(q_rows, np.uint16), _c(w_rows, np.float32), _keys(k, S.key_fp8), \
+        _c(k_scale, np.float32)
+    n = len(rows)
+    idx = np.empty((n, topk), np.int32)
+    val = np.empty((n, topk), np.float64) if with_vals else None
+    _check(lib().orc_topk_flat(ctypes.byref(S), _ptr(q), _ptr(w), _ptr(k), _ptr(ks), topk,
+                               _ptr(rows), n, _ptr(idx), _ptr(val)), "topk_flat")
+    return idx, val
+
+
+def pool(shape: dict, k, k_scale, block):
+    """Pooled keys [batch, n_k // block, dim] as bf16 bits."""
+    S = _shape(**shape)
+    k, ks = _keys(k, S.key_fp8), _c(k_scale, np.float32)
+    out = np.empty((S.batch, S.n_k // block, S.dim), np.uint16)
+    _check(lib().orc_pool(ctypes.byref(S), _ptr(k), _ptr(ks), block, _ptr(out)), "pool")
+    return out
+
+
+def block_select(shape: dict, q_rows, w_rows, pooled, block, m_scored, flags, rows):
+    """(blk int32 [n, m_total], blk_vals float64 [n, m_total])."""
+    S = _shape(**shape)
+    rows = _c(rows, np.int64)
+    m_total = m_scored + bin(flags).count("1")
+    blk = np.empty((len(rows), m_total), np.int32)
+    bv = np.empty((len(rows), m_total), np.float64)
+    _check(lib().orc_block_select(ctypes.byref(S), _ptr(_c(q_rows, np.uint16)),
+                                  _ptr(_c(w_rows, np.float32)), _ptr(_c(pooled, np.uint16)),
+                                  block, m_scored, flags, _ptr(rows), len(rows), m_total,
+                                  _ptr(blk), _ptr(bv)), "block_select")
+    return blk, bv
+
+
+def refine(shape: dict, q_rows, w_rows, k, k_scale, block, blk, topk, rows, with_vals=True):
+    """Top-k within the kept blocks blk [n, m_total] of the listed rows."""
+    S = _shape(**shape)
+    rows = _c(rows, np.int64)
+    blk = _c(blk, np.int32)
+    n = len(rows)
+    idx = np.empty((n, topk), np.int32)
+    val = np.empty((n, topk), np.float64) if with_vals else None
+    _check(lib().orc_refine(ctypes.byref(S), _ptr(_c(q_rows, np.uint16)),
+                            _ptr(_c(w_rows, np.float32)), _ptr(_keys(k, S.key_fp8)),
+                            _ptr(_c(k_scale, np.float32)), block, _ptr(blk), blk.shape[1], topk,
+                            _ptr(rows), n, _ptr(idx), _ptr(val)), "refine")
+    return idx, val
+
+
+def hisa(shape: dict, q_rows, w_rows, k, k_scale, block, m_scored, flags, topk, rows,
+         with_vals=True):
+    """Whole HISA indexer: (blk [n, m_total], idx [n, topk], vals [n, topk] | None)."""
+    S = _shape(**shape)
+    rows = _c(rows, np.int64)
+    n = len(rows)
+    m_total = m_scored + bin(flags).count("1")
+    blk = np.empty((n, m_total), np.int32)
+    idx = np.empty((n, topk), np.int32)
+    val = np.empty((n, topk), np.float64) if with_vals else None
+    _check(lib().orc_hisa(ctypes.byref(S), _ptr(_c(q_rows, np.uint16)),
+                          _ptr(_c(w_rows, np.float32)), _ptr(_keys(k, S.key_fp8)),
+                          _ptr(_c(k_scale, np.float32)), block, m_scored, flags, topk,
+                          _ptr(rows), n, _ptr(blk), _ptr(idx), _ptr(val)), "hisa")
+    return blk, idx, val

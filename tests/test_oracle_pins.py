@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle against facts fixed independently of it.
+
+Each test pins one part of the oracle to something other than the oracle:
+a library routine on a special case (torch's bf16 / e4m3fn casts, numpy
+matmul), a closed form, an invariant of the method, or a brute-force full
+sort on tiny inputs.  The oracle follows the HISA abstract (indexer scoring,
+two-stage block filter + token refinement, per-query top-k interface) and
+the StreamIndex abstract (compressed keys, chunked top-k)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tks_inputs import (FORCE_FIRST, FORCE_LOCAL, bf16_bits_to_fp32, fp32_to_bf16_bits,
+                        fp32_to_e4m3fn)
+
+
+def shp(n_q, n_k, heads, dim, batch=1, q_pos0=0, ratio=1, fp8=0):
+    return dict(batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=dim, q_pos0=q_pos0,
+                causal_ratio=ratio, key_dtype=fp8)
+
+
+def rand_int(rng, shape, lo=-4, hi=4):
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def brute_topk(scores, valid, k):
+    """Full lexsort (score desc, index asc) of one row; -1 padded."""
+    idx = np.nonzero(valid)[0]
+    order = np.lexsort((idx, -scores[idx]))
+    top = idx[order][:k]
+    out = -np.ones(k, np.int64)
+    out[:len(top)] = top
+    return out
+
+
+# ------------------------------------------------------------------ decoders
+
+def test_bf16_decode_matches_torch_for_all_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits[::7]])
+    np.testing.assert_array_equal(got, ref[::7])
+
+
+def test_e4m3fn_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3fn_to_double(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.isnan(got[nan]).all()
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-39).astype(np.float32),      # subnormals
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+        # exact halfway cases: bf16 value + half an ulp (ties to even)
+        (bf16_bits_to_fp32(rng.integers(0x3F00, 0x4100, 500).astype(np.uint16)).view(np.uint32)
+         + np.uint32(0x8000)).view(np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.double_to_bf16(float(v)) for v in x], np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_generator_bf16_and_e4m3_encoders_match_torch():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(20000).astype(np.float32) * 50
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(fp32_to_bf16_bits(x), ref)
+    y = np.clip(x, -448, 448)
+    ref8 = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(fp32_to_e4m3fn(y), ref8)
+
+
+# ------------------------------------------------------------------- scoring
+
+def test_single_head_unit_weight_is_relu_of_matmul():
+    """H=1, w=1: I = max(0, q k^T) -- a plain matrix product on integers."""
+    rng = np.random.default_rng(2)
+    T, D = 48, 32
+    q = rand_int(rng, (1, T, 1, D))
+    k = rand_int(rng, (1, T, D))
+    w = np.ones((1, T, 1), np.float32)
+    got = oracle.index_scores(shp(T, T, 1, D), fp32_to_bf16_bits(q), w, fp32_to_bf16_bits(k),
+                              None, 0, T, 0, T)[0]
+    ref = np.maximum(q[0, :, 0, :].astype(np.float64) @ k[0].T.astype(np.float64), 0.0)
+    causal = np.tril(np.ones((T, T), bool))
+    np.testing.assert_array_equal(got[causal], ref[causal])
+    assert np.all(np.isneginf(got[~causal]))
+
+
+def test_basis_keys_pick_one_coordinate_per_head():
+    """k[s] = e_{d(s)}: I[t,s] = sum_h w[t,h] * max(0, q[t,h,d(s)])."""
+    rng = np.random.default_rng(3)
+    T, H, D = 40, 3, 16
+    q = rand_int(rng, (1, T, H, D))
+    w = rand_int(rng, (1, T, H))
+    d_of_s = rng.integers(0, D, T)
+    k = np.zeros((1, T, D), np.float32)
+    k[0, np.arange(T), d_of_s] = 1.0
+    got = oracle.index_scores(shp(T, T, H, D, q_pos0=T), fp32_to_bf16_bits(q), w,
+                              fp32_to_bf16_bits(k), None, 0, T, 0, T)[0]
+    for t in range(T):
+        for s in range(T):
+            want = sum(float(w[0, t, h]) * max(0.0, float(q[0, t, h, d_of_s[s]])) for h in range(H))
+            assert got[t, s] == want
+
+
+def test_one_hot_head_weight_selects_that_head():
+    rng = np.random.default_rng(4)
+    T, H, D = 32, 4, 8
+    q = rand_int(rng, (1, T, H, D))
+    k = rand_int(rng, (1, T, D))
+    for h in range(H):
+        w = np.zeros((1, T, H), np.float32)
+        w[..., h] = 1.0
+        got = oracle.index_scores(shp(T, T, H, D, q_pos0=T), fp32_to_bf16_bits(q), w,
+                                  fp32_to_bf16_bits(k), None, 0, T, 0, T)[0]
+        ref = np.maximum(q[0, :, h, :].astype(np.float64) @ k[0].T.astype(np.float64), 0)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_head_permutation_invariance_and_weight_linearity():
+    rng = np.random.default_rng(5)
+    T, H, D = 24, 5, 8
+    q = rand_int(rng, (1, T, H, D))
+    k = rand_int(rng, (1, T, D))
+    w = rand_int(rng, (1, T, H))
+    S = shp(T, T, H, D)
+    base = oracle.index_scores(S, fp32_to_bf16_bits(q), w, fp32_to_bf16_bits(k), None, 0, T, 0, T)
+    perm = rng.permutation(H)
+    p = oracle.index_scores(S, fp32_to_bf16_bits(q[:, :, perm]), w[:, :, perm],
+                            fp32_to_bf16_bits(k), None, 0, T, 0, T)
+    np.testing.assert_array_equal(base, p)
+    two = oracle.index_scores(S, fp32_to_bf16_bits(q), 2 * w, fp32_to_bf16_bits(k), None,
+                              0, T, 0, T)
+    fin = np.isfinite(base)
+    np.testing.assert_array_equal(two[fin], 2 * base[fin])
+
+
+def test_all_dots_negative_gives_zero_score_even_with_negative_weights():
+    T, H, D = 16, 2, 4
+    q = np.ones((1, T, H, D), np.float32)
+    k = -np.ones((1, T, D), np.float32)
+    w = -np.ones((1, T, H), np.float32)
+    got = oracle.index_scores(shp(T, T, H, D), fp32_to_bf16_bits(q), w, fp32_to_bf16_bits(k),
+                              None, 0, T, 0, T)[0]
+    causal = np.tril(np.ones((T, T), bool))
+    assert np.all(got[causal] == 0.0) and not np.any(np.signbit(got[causal]))
+
+
+def test_fp8_keys_equal_bf16_keys_with_same_values():
+    """scale * e4m3 values that bf16 holds exactly score like bf16 keys."""
+    rng = np.random.default_rng(6)
+    T, H, D = 32, 3, 16
+    q = rand_int(rng, (1, T, H, D))
+    w = rand_int(rng, (1, T, H))
+    vals = rand_int(rng, (1, T, D), -8, 8)          # integers are exact in e4m3
+    codes = fp32_to_e4m3fn(vals)
+    scale = np.full((1, T), 0.25, np.float32)       # power of two keeps it exact
+    got = oracle.index_scores(shp(T, T, H, D, fp8=1), fp32_to_bf16_bits(q), w, codes, scale,
+                              0, T, 0, T)
+    ref = oracle.index_scores(shp(T, T, H, D), fp32_to_bf16_bits(q), w,
+                              fp32_to_bf16_bits(vals * 0.25), None, 0, T, 0, T)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("q_pos0,ratio", [(0, 1), (5, 1), (0, 4), (-3, 4), (-100, 1)])
+def test_visibility_counts(q_pos0, ratio):
+    S = shp(64, 20, 1, 4, q_pos0=q_pos0, ratio=ratio)
+    for t in range(64):
+        pos = q_pos0 + t
+        vis = pos // ratio                      # python floor division
+        want = 0 if vis < 0 else min(vis + 1, 20)
+        assert oracle.n_visible(S, t) == want
+
+
+def test_future_keys_never_selected():
+    """Keys after the query are made huge; the causal mask must still skip them."""
+    rng = np.random.default_rng(7)
+    T, H, D, K = 64, 2, 8, 8
+    q = np.abs(rand_int(rng, (1, T, H, D))) + 1
+    w = np.ones((1, T, H), np.float32)
+    k = rand_int(rng, (1, T, D))
+    idx, _ = oracle.topk_flat(shp(T, T, H, D), fp32_to_bf16_bits(q[0]), w[0],
+                              fp32_to_bf16_bits(k), None, K, np.arange(T))
+    k_big = k.copy()
+    for t in range(T):
+        kk = k_big.copy()
+        kk[0, t + 1:] = 100.0
+        i2, _ = oracle.topk_flat(shp(T, T, H, D), fp32_to_bf16_bits(q[0, t:t + 1]),
+                                 w[0, t:t + 1], fp32_to_bf16_bits(kk), None, K, [t])
+        np.testing.assert_array_equal(i2[0], idx[t])
+        assert np.all(i2[0][i2[0] >= 0] <= t)
+
+
+# --------------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("seed,k", [(10, 5), (11, 16), (12, 64), (13, 100)])
+def test_topk_equals_brute_force_full_sort(seed, k):
+    rng = np.random.default_rng(seed)
+    T, H, D = 96, 3, 8
+    q = rand_int(rng, (1, T, H, D), -2, 2)          # small range: many exact ties
+    w = rand_int(rng, (1, T, H), -2, 2)
+    kk = rand_int(rng, (1, T, D), -2, 2)
+    S = shp(T, T, H, D)
+    sc = oracle.index_scores(S, fp32_to_bf16_bits(q), w, fp32_to_bf16_bits(kk), None, 0, T, 0, T)[0]
+    idx, val = oracle.topk_flat(S, fp32_to_bf16_bits(q[0]), w[0], fp32_to_bf16_bits(kk), None, k,
+                                np.arange(T))
+    for t in range(T):
+        want = brute_topk(sc[t], np.isfinite(sc[t]), k)
+        np.testing.assert_array_equal(idx[t], want)
+        ok = want >= 0
+        np.testing.assert_array_equal(val[t][ok], sc[t][want[ok]])
+        assert np.all(np.isnan(val[t][~ok]))
+
+
+def test_all_equal_scores_give_lowest_indices():
+    T, H, D, K = 200, 2, 4, 64
+    q = np.zeros((T, H, D), np.float32)
+    w = np.ones((T, H), np.float32)
+    k = np.ones((1, T, D), np.float32)
+    idx, val = oracle.topk_flat(shp(T, T, H, D), fp32_to_bf16_bits(q), w, fp32_to_bf16_bits(k),
+                                None, K, np.arange(T))
+    for t in range(T):
+        n = min(K, t + 1)
+        np.testing.assert_array_equal(idx[t, :n], np.arange(n))
+        assert np.all(idx[t, n:] == -1) and np.all(val[t, :n] == 0.0)
+
+
+def test_planted_maxima_come_first():
+    rng = np.random.default_rng(8)
+    T, H, D, K = 128, 2, 8, 10
+    q = np.ones((1, 1, H, D), np.float32)
+    k = rand_int(rng, (1, T, D), -1, 1)
+    planted = [3, 77, 100, 127]
+    for j, s in enumerate(planted):
+        k[0, s] = 4.0 - j * 0.5                      # decreasing planted scores
+    w = np.ones((1, 1, H), np.float32)
+    idx, _ = oracle.topk_flat(shp(1, T, H, D, q_pos0=T - 1), fp32_to_bf16_bits(q[0]), w[0],
+                              fp32_to_bf16_bits(k), None, K, [0])
+    np.testing.assert_array_equal(idx[0, :4], planted)
+
+
+# ----------------------------------------------------------------- pooling
+
+def test_pool_of_integers_is_exact_mean():
+    rng = np.random.default_rng(9)
+    T, D, B = 256, 16, 64
+    k = rand_int(rng, (2, T, D))
+    got = oracle.pool(shp(1, T, 1, D, batch=2), fp32_to_bf16_bits(k), None, B)
+    ref = k.reshape(2, T // B, B, D).astype(np.float64).mean(axis=2)
+    np.testing.assert_array_equal(bf16_bits_to_fp32(got).astype(np.float64), ref)
+
+
+def _nearest_bf16_ok(bits, exact):
+    """bits is a nearest bf16 of `exact` (no other bf16 value is strictly closer)."""
+    v = bf16_bits_to_fp32(bits).astype(np.float64)
+    up = bf16_bits_to_fp32((bits.astype(np.int32) + 1).astype(np.uint16)).astype(np.float64)
+    dn = bf16_bits_to_fp32((bits.astype(np.int32) - 1).astype(np.uint16)).astype(np.float64)
+    err = np.abs(v - exact)
+    return np.all(err <= np.abs(up - exact)) and np.all(err <= np.abs(dn - exact))
+
+
+def test_pool_of_floats_is_nearest_bf16_of_mean_and_ignores_tail():
+    rng = np.random.default_rng(10)
+    T, D, B = 1000, 8, 128                           # 7 complete blocks + a 104-key tail
+    k = fp32_to_bf16_bits(rng.standard_normal((1, T, D)).astype(np.float32))
+    got = oracle.pool(shp(1, T, 1, D), k, None, B)
+    assert got.shape == (1, T // B, D)
+    kv = bf16_bits_to_fp32(k).astype(np.float64)
+    exact = kv[:, :7 * B].reshape(1, 7, B, D).mean(axis=2)
+    assert _nearest_bf16_ok(got, exact)
+    np.testing.assert_allclose(bf16_bits_to_fp32(got), exact, rtol=2 ** -8)
+
+
+def test_pool_fp8_uses_dequantised_keys():
+    rng = np.random.default_rng(11)
+    T, D, B = 256, 8, 64
+    codes = rng.integers(0, 256, (1, T, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10            # no NaN codes
+    scale = (rng.random((1, T)) * 0.01 + 1e-3).astype(np.float32)
+    got = oracle.pool(shp(1, T, 1, D, fp8=1), codes, scale, B)
+    deq = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy() * \
+        scale.astype(np.float64)[..., None]
+    exact = deq.reshape(1, T // B, B, D).mean(axis=2)
+    assert _nearest_bf16_ok(got, exact)
+
+
+# ----------------------------------------------------------- block selection
+
+def _int_case(seed, T=256, H=2, D=8):
+    rng = np.random.default_rng(seed)
+    q = rand_int(rng, (1, T, H, D))
+    w = rand_int(rng, (1, T, H))
+    k = rand_int(rng, (1, T, D))
+    return fp32_to_bf16_bits(q), w, fp32_to_bf16_bits(k)
+
+
+def test_hisa_with_every_block_kept_equals_flat():
+    """HISA abstract, stage (2): the original indexer on the retained blocks;
+    keeping every block must therefore reproduce the flat top-k exactly."""
+    T, H, D, B, K = 256, 2, 8, 16, 12
+    q, w, k = _int_case(12, T, H, D)
+    S = shp(T, T, H, D)
+    rows = np.arange(T)
+    fi, fv = oracle.topk_flat(S, q[0], w[0], k, None, K, rows)
+    for flags in (FORCE_LOCAL, FORCE_FIRST | FORCE_LOCAL):
+        blk, hi, hv = oracle.hisa(S, q[0], w[0], k, None, B, T // B, flags, K, rows)
+        np.testing.assert_array_equal(hi, fi)
+        np.testing.assert_array_equal(hv, fv)
+
+
+def test_block_size_one_selects_the_flat_top_m_tokens():
+    """With B = 1 the pooled keys are the keys; the scored blocks of query t
+    are its best m keys among 0..t-1 (flat top-m with one key less visible)."""
+    T, H, D, M = 96, 2, 8, 7
+    q, w, k = _int_case(13, T, H, D)
+    rows = np.arange(T)
+    pooled = oracle.pool(shp(T, T, H, D), k, None, 1)
+    np.testing.assert_array_equal(pooled, k)
+    blk, bv = oracle.block_select(shp(T, T, H, D), q[0], w[0], pooled, 1, M, FORCE_LOCAL, rows)
+    fi, fv = oracle.topk_flat(shp(T, T, H, D, q_pos0=-1), q[0], w[0], k, None, M, rows)
+    for t in range(T):
+        got = blk[t][blk[t] >= 0]
+        assert t in got                                   # local block forced
+        scored = sorted(set(got.tolist()) - {t})
+        want = sorted(x for x in fi[t].tolist() if x >= 0)
+        assert scored == want
+        np.testing.assert_array_equal(got, np.sort(got))   # ascending
+        assert np.all(bv[t][blk[t] == t] == np.inf)
+
+
+def test_block_select_forced_blocks_and_padding():
+    T, H, D, B, M = 512, 2, 8, 32, 3
+    q, w, k = _int_case(14, T, H, D)
+    rows = np.arange(T)
+    pooled = oracle.pool(shp(T, T, H, D), k, None, B)
+    blk, bv = oracle.block_select(shp(T, T, H, D), q[0], w[0], pooled, B, M,
+                                  FORCE_FIRST | FORCE_LOCAL, rows)
+    assert blk.shape == (T, M + 2)
+    for t in range(T):
+        L = t // B
+        got = blk[t][blk[t] >= 0]
+        assert L in got and 0 in got
+        n_eligible = max(0, L - 1)                         # blocks 1..L-1
+        assert len(got) == min(M, n_eligible) + (2 if L > 0 else 1)
+        assert np.all(got <= L)
+        assert np.all(blk[t][len(got):] == -1)
+
+
+def test_planted_block_is_selected():
+    rng = np.random.default_rng(15)
+    T, H, D, B = 1024, 2, 8, 64
+    q = np.ones((1, H, D), np.float32)
+    w = np.ones((1, H), np.float32)
+    k = rand_int(rng, (1, T, D), -1, 1)
+    k[0, 5 * B:6 * B] = 3.0
+    S = shp(1, T, H, D, q_pos0=T - 1)
+    pooled = oracle.pool(S, fp32_to_bf16_bits(k), None, B)
+    blk, bv = oracle.block_select(S, fp32_to_bf16_bits(q), w, pooled, B, 1, FORCE_LOCAL, [0])
+    assert blk[0].tolist() == [5, 15]
+
+
+def test_refine_equals_brute_force_on_kept_blocks():
+    T, H, D, B, K = 192, 2, 8, 16, 20
+    q, w, k = _int_case(16, T, H, D)
+    S = shp(T, T, H, D)
+    rows = np.arange(T)
+    rng = np.random.default_rng(17)
+    blk = -np.ones((T, 4), np.int32)
+    for t in range(T):
+        L = t // B
+        chosen = np.sort(rng.choice(L + 1, size=min(4, L + 1), replace=False))
+        blk[t, :len(chosen)] = chosen
+    idx, val = oracle.refine(S, q[0], w[0], k, None, B, blk, K, rows)
+    sc = oracle.index_scores(S, q, w[None, 0] if w.ndim == 2 else w, k, None, 0, T, 0, T)[0]
+    for t in range(T):
+        keep = np.zeros(T, bool)
+        for b in blk[t]:
+            if b >= 0:
+                keep[b * B:(b + 1) * B] = True
+        want = brute_topk(sc[t], keep & np.isfinite(sc[t]), K)
+        np.testing.assert_array_equal(idx[t], want)
+
+
+def test_materialized_score_tensor_size_is_256_gib():
+    """StreamIndex abstract: [B, S, H_I, T] fp32 with H_I = 64, m = 4 is 256 GB
+    at S = 65,536 (2^16 * 64 * 2^14 * 4 bytes = 2^38 bytes)."""
+    S, H, m = 65536, 64, 4
+    assert S * H * (S // m) * 4 == 2 ** 38
