@@ -1,0 +1,182 @@
+/*
+ * tks.h -- C ABI of the MI355X (gfx950) sparse-attention indexer + top-k.
+ *
+ * The operation (HISA abstract; StreamIndex abstract):
+ *   a lightweight indexer with H indexer heads scores every causal key s for
+ *   every query t as
+ *       I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:])
+ *   and keeps, per query, the k best key indices.  The flat (DSA-style) form
+ *   scans every visible key; the HISA form mean-pools keys into blocks,
+ *   scores the pooled representatives, keeps the best blocks and runs the
+ *   same token indexer only inside them.  Both emit the same per-query top-k
+ *   index set.  Selection is streamed over query chunks and key tiles with a
+ *   partition-merge of partial top-k lists, so no [queries x keys] score
+ *   tensor is ever allocated.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers unless stated; the caller allocates and
+ *     owns every buffer, including workspaces (sized by the *_workspace
+ *     queries).  The library never allocates device memory.
+ *   - All calls are asynchronous on `stream`; inputs must stay alive and
+ *     unmodified until the stream reaches the end of the call.
+ *   - Layouts are dense row-major as annotated.  q, k and pooled keys are
+ *     16-byte aligned; score buffers, idx and vals 4-byte aligned.
+ *   - q is bf16 [batch, n_q, heads, dim]; w is fp32 [batch, n_q, heads];
+ *     k is bf16 [batch, n_k, dim], or OCP e4m3fn codes [batch, n_k, dim]
+ *     with a per-token fp32 scale k_scale [batch, n_k] (key value =
+ *     scale * e4m3fn(code), scale >= 0).  Inputs must be finite.
+ *   - Visibility: key s is seen by query t iff s <= floor((q_pos0 + t) /
+ *     causal_ratio) and s < n_k.  q_pos0 = 0 for prefill, n_k - 1 for one
+ *     decode token; causal_ratio > 1 is causality at compressed-key
+ *     granularity (one key per causal_ratio positions).
+ *   - Output rows hold the min(topk, candidates) best keys ordered by score
+ *     descending, then key index ascending (-0 equals +0), then -1 (idx) /
+ *     NaN (vals) padding.  This order is a total order, so the result is
+ *     unique.
+ *   - Supported: 1 <= heads <= 64, dim in {32, 64, 128}, 1 <= topk <= 2048,
+ *     HISA block in {32, 64, 128, 256}.  Sizes outside return
+ *     TKS_EUNSUPPORTED; malformed arguments return TKS_EINVAL; a workspace
+ *     smaller than the query returns TKS_EWORKSPACE; a failed launch returns
+ *     TKS_EHIP.  Arguments are checked before anything is launched, and a
+ *     non-OK status leaves outputs untouched.  tks_last_error() then gives
+ *     a thread-local message.  Device faults surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef TKS_H
+#define TKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TKS_OK = 0,
+    TKS_EINVAL = -1,
+    TKS_EUNSUPPORTED = -2,
+    TKS_EWORKSPACE = -3,
+    TKS_EHIP = -4
+} tks_status;
+
+typedef enum { TKS_KEY_BF16 = 0, TKS_KEY_FP8_E4M3FN = 1 } tks_key_dtype;
+
+/* HISA forced blocks: block 0 and the query's local block (the block that
+ * holds its last visible key). */
+enum { TKS_FORCE_FIRST = 1u, TKS_FORCE_LOCAL = 2u };
+
+typedef struct {
+    int32_t batch;        /* independent sequences                         */
+    int32_t n_q;          /* queries per sequence                          */
+    int32_t n_k;          /* keys per sequence                             */
+    int32_t heads;        /* indexer heads H                               */
+    int32_t dim;          /* indexer head dimension D                      */
+    int32_t q_pos0;       /* position of query 0                           */
+    int32_t causal_ratio; /* positions per key (1 = token-level causality) */
+    int32_t key_dtype;    /* tks_key_dtype                                 */
+} tks_shape;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int tks_version(void);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* tks_last_error(void);
+
+/*
+ * Raw indexer scores of a rectangle of (query, key) pairs -- the tile-sized
+ * "materialise" step of the StreamIndex abstract, kept for testing and
+ * debugging (the top-k calls below never need it).
+ *   scores: fp32 [batch, q_count, k_count]; scores[b, i, j] = I[q_begin + i,
+ *   k_begin + j] of sequence b, or -inf where the key is not visible.
+ * Requires 0 <= q_begin, q_begin + q_count <= n_q, 0 <= k_begin,
+ * k_begin + k_count <= n_k.
+ */
+int tks_indexer_scores(const tks_shape* shape, const void* q, const float* w, const void* k,
+                       const float* k_scale, int32_t q_begin, int32_t q_count, int32_t k_begin,
+                       int32_t k_count, float* scores, hipStream_t stream);
+
+/*
+ * Flat (DSA-style) indexer top-k over every visible key (HISA abstract:
+ * the flat token scan it replaces; StreamIndex abstract: chunked
+ * partition-merge top-k).  Query rows are processed in chunks of q_chunk
+ * rows; keys in tiles of k_tile keys; each tile's partial top-k is merged
+ * into a running per-row list.  q_chunk = 0 / k_tile = 0 pick sizes
+ * automatically.  The result does not depend on q_chunk or k_tile.
+ *   idx:  int32 [batch, n_q, topk];  vals: fp32 [batch, n_q, topk] or NULL.
+ * The workspace size depends only on (shape, topk, q_chunk, k_tile).
+ */
+size_t tks_topk_flat_workspace(const tks_shape* shape, int32_t topk, int32_t q_chunk,
+                               int32_t k_tile);
+int tks_topk_flat(const tks_shape* shape, const void* q, const float* w, const void* k,
+                  const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                  int32_t* idx, float* vals, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * Top-k of rows of a score matrix that is already in device memory (the
+ * selection stage on its own).  Row r holds row_len[r] valid scores at
+ * scores + r * row_stride (row_len NULL: n_cols for every row); candidate j
+ * of a row is key index j.  Scores must not be NaN.
+ *   idx / vals: [n_rows, topk] (vals may be NULL).
+ */
+size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk);
+int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,
+                    const int32_t* row_len, int32_t topk, int32_t* idx, float* vals,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * HISA block pooling (HISA abstract, stage (1): pooled block
+ * representatives): pooled[b, j, :] = bf16 nearest-even rounding of the mean
+ * of keys j*block .. j*block+block-1 (fp8 keys dequantised first), summed in
+ * double in ascending key order.  Only the n_k / block complete blocks are
+ * written.
+ *   pooled: bf16 [batch, n_k / block, dim].
+ */
+int tks_hisa_pool_keys(const tks_shape* shape, const void* k, const float* k_scale,
+                       int32_t block, void* pooled, hipStream_t stream);
+
+/*
+ * HISA block selection (HISA abstract, stage (1): score the pooled block
+ * representatives with the indexer and discard irrelevant regions).  For
+ * query t with local block L (the block holding its last visible key):
+ * forced blocks are L (TKS_FORCE_LOCAL) and 0 (TKS_FORCE_FIRST, when
+ * L > 0); the complete blocks j < L that are not forced are scored as
+ * I_blk[t,j] = sum_h w[t,h] * max(0, q[t,h,:] . pooled[j,:]) and the
+ * m_scored best (score desc, block asc) are kept.
+ *   blk:      int32 [batch, n_q, m_total], kept blocks ascending, -1 padded.
+ *   blk_vals: fp32 same shape or NULL; block score, +inf for forced blocks,
+ *             NaN for padding.
+ *   m_total must equal m_scored + popcount(force_flags) (1 <= m_total <= 512,
+ *   m_scored <= 2048).
+ */
+size_t tks_hisa_block_select_workspace(const tks_shape* shape, int32_t block, int32_t m_scored);
+int tks_hisa_block_select(const tks_shape* shape, const void* q, const float* w,
+                          const void* pooled, int32_t block, int32_t m_scored,
+                          uint32_t force_flags, int32_t* blk, float* blk_vals, int32_t m_total,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * HISA token refinement (HISA abstract, stage (2): the original indexer
+ * applied only within the retained candidate blocks; same top-k interface
+ * as the flat scan).  Candidates of query t are the visible keys of the
+ * blocks listed in its row of blk (ascending, distinct, -1 entries
+ * ignored, as tks_hisa_block_select writes them).  q_chunk = 0 picks the
+ * row chunk automatically.
+ *   idx / vals: as for tks_topk_flat.
+ */
+size_t tks_hisa_refine_workspace(const tks_shape* shape, int32_t block, int32_t m_total,
+                                 int32_t topk, int32_t q_chunk);
+int tks_hisa_refine_topk(const tks_shape* shape, const void* q, const float* w, const void* k,
+                         const float* k_scale, int32_t block, const int32_t* blk,
+                         int32_t m_total, int32_t topk, int32_t q_chunk, int32_t* idx,
+                         float* vals, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TKS_H */

@@ -62,6 +62,7 @@ def lib():
         L.orc_n_visible.restype = i64
         L.orc_index_scores.argtypes = [SP, P, P, P, P, i32, i32, i32, i32, P]
         L.orc_topk_flat.argtypes = [SP, P, P, P, P, i32, P, i64, P, P]
+        L.orc_row_scores.argtypes = [SP, P, P, P, P, P, i64, P]
         L.orc_pool.argtypes = [SP, P, P, i32, P]
         L.orc_block_select.argtypes = [SP, P, P, P, i32, i32, u32, P, i64, i32, P, P]
         L.orc_refine.argtypes = [SP, P, P, P, P, i32, P, i32, i32, P, i64, P, P]
@@ -121,6 +122,19 @@ def index_scores(shape: dict, q, w, k, k_scale, q_begin, q_count, k_begin, k_cou
     out = np.empty((S.batch, q_count, k_count), np.float64)
     _check(lib().orc_index_scores(ctypes.byref(S), _ptr(q), _ptr(w), _ptr(k), _ptr(ks),
                                   q_begin, q_count, k_begin, k_count, _ptr(out)), "index_scores")
+    return out
+
+
+def row_scores(shape: dict, q_rows, w_rows, k, k_scale, rows):
+    """[n, n_k] float64 scores of every key for the listed rows (-inf where not
+    visible).  q_rows / w_rows hold the listed rows only."""
+    S = _shape(**shape)
+    rows = _c(rows, np.int64)
+    out = np.empty((len(rows), S.n_k), np.float64)
+    _check(lib().orc_row_scores(ctypes.byref(S), _ptr(_c(q_rows, np.uint16)),
+                                _ptr(_c(w_rows, np.float32)), _ptr(_keys(k, S.key_fp8)),
+                                _ptr(_c(k_scale, np.float32)), _ptr(rows), len(rows),
+                                _ptr(out)), "row_scores")
     return out
 
 

@@ -207,6 +207,11 @@ int orc_index_scores(const orc_shape* S, const uint16_t* q, const float* w, cons
     return 0;
 }
 
+/* Scores of every key for the listed rows (q / w hold those rows only);
+ * keys a query cannot see get -inf.  out: [n_rows, n_k]. */
+int orc_row_scores(const orc_shape* S, const uint16_t* q, const float* w, const void* k,
+                   const float* k_scale, const int64_t* rows, int64_t n_rows, double* out);
+
 /* --------------------------------------------------------------- ordering */
 
 typedef struct {
@@ -241,6 +246,21 @@ static void emit_topk(orc_entry* cand, int64_t n, int32_t topk, int32_t* idx, do
 static int check_rows(const orc_shape* S, const int64_t* rows, int64_t n_rows) {
     for (int64_t i = 0; i < n_rows; ++i)
         if (rows[i] < 0 || rows[i] >= (int64_t)S->batch * S->n_q) return -1;
+    return 0;
+}
+
+int orc_row_scores(const orc_shape* S, const uint16_t* q, const float* w, const void* k,
+                   const float* k_scale, const int64_t* rows, int64_t n_rows, double* out) {
+    if (check_shape(S) || check_rows(S, rows, n_rows)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t b = rows[i] / S->n_q, t = rows[i] % S->n_q;
+        int64_t nv = orc_n_visible(S, t);
+        for (int64_t s = 0; s < S->n_k; ++s)
+            out[i * S->n_k + s] = s < nv ? score_key(S, q + i * S->heads * S->dim,
+                                                     w + i * S->heads, k, k_scale, b, s)
+                                         : -INFINITY;
+    }
     return 0;
 }
 

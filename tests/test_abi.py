@@ -1,0 +1,139 @@
+"""C ABI contract, checked on the CPU: the library loads without a GPU, it
+exports every function include/tks.h declares, and each malformed or
+unsupported argument returns its documented status before any launch (no
+call here reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from top_key_selection_amd import tks
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+EINVAL, EUNSUP, EWS = tks.EINVAL, tks.EUNSUPPORTED, tks.EWORKSPACE
+A = ctypes.c_void_p(4096)        # aligned fake device address (never dereferenced)
+MIS = ctypes.c_void_p(4096 + 2)  # misaligned fake address
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "tks.h")).read()
+    return sorted(set(re.findall(r"\b(tks_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = tks.lib()
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tks.SYMBOLS)
+
+
+def test_version_and_empty_error():
+    assert tks.version() >= 100
+
+
+def S(**kw):
+    base = dict(batch=1, n_q=16, n_k=16, heads=4, dim=32)
+    base.update(kw)
+    return tks.Shape(**base).c()
+
+
+def flat(shape, q=A, w=A, k=A, ks=None, topk=4, qc=0, kt=0, idx=A, vals=None, ws=A, wsb=1 << 30):
+    return tks.lib().tks_topk_flat(ctypes.byref(shape), q, w, k, ks, topk, qc, kt, idx, vals, ws,
+                                   wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads=0), EUNSUP), (dict(heads=65), EUNSUP), (dict(dim=48), EUNSUP),
+    (dict(dim=256), EUNSUP), (dict(causal_ratio=0), EINVAL), (dict(n_q=-1), EINVAL),
+    (dict(key_dtype=7), EINVAL), (dict(batch=1 << 20, n_q=1 << 12), EUNSUP),
+])
+def test_flat_rejects_bad_shapes(kw, code):
+    assert flat(S(**kw)) == code
+    assert tks.last_error()
+
+
+def test_flat_rejects_bad_arguments():
+    s = S()
+    assert flat(s, topk=0) == EUNSUP
+    assert flat(s, topk=2049) == EUNSUP
+    assert flat(s, q=None) == EINVAL
+    assert flat(s, w=None) == EINVAL
+    assert flat(s, k=None) == EINVAL
+    assert flat(s, idx=None) == EINVAL
+    assert flat(s, q=MIS) == EINVAL
+    assert flat(s, k=MIS) == EINVAL
+    assert flat(s, kt=33) == EINVAL
+    assert flat(s, qc=-1) == EINVAL
+    assert flat(S(key_dtype=1)) == EINVAL          # fp8 keys without scales
+    assert flat(s, ws=None) == EWS
+    assert flat(s, wsb=0) == EWS
+    assert flat(s, ws=MIS) == EINVAL
+    assert "workspace" in (flat(s, wsb=1) and tks.last_error())
+
+
+def test_empty_problem_is_ok_without_launch():
+    assert flat(S(n_q=0), q=None, w=None, k=None, idx=None) == tks.OK
+    assert flat(S(batch=0), q=None, w=None, k=None, idx=None) == tks.OK
+
+
+def test_workspace_queries():
+    s = tks.Shape(1, 8192, 8192, 64, 128)
+    assert tks.topk_flat_workspace(s, 2048) >= 8192 * 4
+    # tiled plans carry the running top-k lists
+    tiled = tks.topk_flat_workspace(s, 2048, q_chunk=1024, k_tile=2048)
+    assert tiled == 1024 * 2048 * 4 + 2 * 1024 * 2048 * 4
+    s5 = tks.Shape(1, 262144, 65536, 64, 128, causal_ratio=4)
+    ws5 = tks.topk_flat_workspace(s5, 2048, 4096, 8192)
+    assert ws5 == 4096 * 8192 * 4 + 2 * 4096 * 2048 * 4   # O(q_chunk * (k_tile + k))
+    full = tks.materialized_score_bytes(1, 262144, 64, 65536)
+    assert ws5 * 1000 < full
+    assert tks.topk_flat_workspace(tks.Shape(1, 8, 8, 0, 32), 4) == 0   # invalid -> 0
+
+
+def test_materialized_score_size_matches_pages():
+    # StreamIndex abstract: [B,S,H_I,T] fp32 at S=65,536, H_I=64, T=S/4 is 256 GB
+    assert tks.materialized_score_bytes(1, 65536, 64, 65536 // 4) == 2 ** 38
+
+
+def test_scores_rejects():
+    L = tks.lib()
+    s = S()
+    f = lambda *a: L.tks_indexer_scores(ctypes.byref(s), *a, None)
+    assert f(A, A, A, None, 0, 17, 0, 4, A) == EINVAL      # q range past n_q
+    assert f(A, A, A, None, 0, 4, 10, 7, A) == EINVAL      # k range past n_k
+    assert f(A, A, A, None, 0, 4, 0, 4, None) == EINVAL    # no output
+    assert f(A, A, A, None, 0, 0, 0, 4, None) == tks.OK    # empty rectangle
+
+
+def test_topk_scores_rejects():
+    L = tks.lib()
+    f = lambda *a: L.tks_topk_scores(*a, None, 0, None)
+    assert f(A, 4, 8, 4, None, 2, A, None) == EINVAL       # stride < n_cols
+    assert f(A, 4, 8, 8, None, 0, A, None) == EUNSUP
+    assert f(None, 4, 8, 8, None, 2, A, None) == EINVAL
+    assert f(A, 0, 8, 8, None, 2, None, None) == tks.OK
+
+
+def test_hisa_rejects():
+    L = tks.lib()
+    s = S(n_k=256)
+    pool = lambda blk, k=A, ks=None, out=A: L.tks_hisa_pool_keys(ctypes.byref(s), k, ks, blk, out, None)
+    assert pool(48) == EUNSUP
+    assert pool(100) == EUNSUP
+    assert pool(64, out=None) == EINVAL
+    assert pool(64, k=MIS) == EINVAL
+    sel = lambda blk, m, flags, mt, ws=A, wsb=1 << 30: L.tks_hisa_block_select(
+        ctypes.byref(s), A, A, A, blk, m, flags, A, None, mt, ws, wsb, None)
+    assert sel(64, 4, 2, 4) == EINVAL          # m_total must count the forced block
+    assert sel(64, 4, 4, 5) == EINVAL          # unknown flag
+    assert sel(64, 600, 0, 600) == EUNSUP      # too many blocks
+    assert sel(64, 4, 2, 5, ws=None) == EWS
+    ref = lambda blk, mt, topk: L.tks_hisa_refine_topk(ctypes.byref(s), A, A, A, None, blk, A, mt,
+                                                       topk, 0, A, None, A, 1 << 30, None)
+    assert ref(64, 0, 4) == EUNSUP
+    assert ref(64, 4, 0) == EUNSUP
+    assert ref(96, 4, 4) == EUNSUP

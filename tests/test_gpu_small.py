@@ -1,0 +1,328 @@
+"""GPU parity on small inputs: exact on integer-valued inputs (fp32 scores are
+exact, so indices and values must equal the oracle's), edge cases, chunk /
+tile / top-k sweeps (the StreamIndex abstract's three sweep axes; results
+must not depend on them), the HISA all-blocks-kept invariant, and the fp8
+e4m3fn decode of every code."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_topk_exact, cfg_rows, check_topk_float, dev, host
+from tks_inputs import (CONFIGS, FORCE_FIRST, FORCE_LOCAL, KEY_FP8, Config, fp32_to_bf16_bits,
+                        fp32_to_e4m3fn, make_inputs, scaled)
+from top_key_selection_amd import tks
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def int_case(seed, batch=1, n_q=256, n_k=256, heads=4, dim=32, lo=-4, hi=4, q_pos0=0, ratio=1,
+             fp8=False):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(lo, hi + 1, (batch, n_q, heads, dim)).astype(np.float32)
+    w = rng.integers(lo, hi + 1, (batch, n_q, heads)).astype(np.float32)
+    kv = rng.integers(lo, hi + 1, (batch, n_k, dim)).astype(np.float32)
+    x = dict(q=fp32_to_bf16_bits(q), w=w)
+    if fp8:
+        x["k"] = fp32_to_e4m3fn(kv)                         # small integers are exact codes
+        x["k_scale"] = (2.0 ** rng.integers(-3, 2, (batch, n_k))).astype(np.float32)
+    else:
+        x["k"] = fp32_to_bf16_bits(kv)
+        x["k_scale"] = None
+    shape = dict(batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=dim, q_pos0=q_pos0,
+                 causal_ratio=ratio, key_dtype=int(fp8))
+    return shape, x
+
+
+def gpu_inputs(x):
+    return dev(x["q"]), dev(x["w"]), dev(x["k"]), dev(x["k_scale"])
+
+
+def oracle_flat(shape, x, topk):
+    R = shape["batch"] * shape["n_q"]
+    rows = np.arange(R)
+    q = x["q"].reshape(R, shape["heads"], shape["dim"])
+    w = x["w"].reshape(R, shape["heads"])
+    return oracle.topk_flat(shape, q, w, x["k"], x["k_scale"], topk, rows)
+
+
+def gpu_flat(shape, x, topk, q_chunk=0, k_tile=0):
+    q, w, k, ks = gpu_inputs(x)
+    idx, vals = tks.topk_flat(tks.Shape(**shape), q, w, k, ks, topk, q_chunk, k_tile)
+    torch.cuda.synchronize()
+    R = shape["batch"] * shape["n_q"]
+    return host(idx).reshape(R, topk), host(vals).reshape(R, topk)
+
+
+# ------------------------------------------------------------ tiny integer
+
+def test_tiny_integer_workload_flat_exact():
+    cfg = CONFIGS[1]
+    say("tiny integer flat L=1024 H=4 D=32 k=64")
+    x = make_inputs(cfg)
+    sh = cfg.shape_dict()
+    oi, ov = oracle_flat(sh, x, cfg.topk)
+    gi, gv = gpu_flat(sh, x, cfg.topk)
+    assert_topk_exact(gi, gv, oi, ov, "tiny flat")
+
+
+def test_tiny_integer_scores_exact():
+    cfg = CONFIGS[1]
+    say("tiny integer indexer_scores")
+    x = make_inputs(cfg)
+    sh = cfg.shape_dict()
+    q, w, k, ks = gpu_inputs(x)
+    for (q0, qn, k0, kn) in [(0, 1024, 0, 1024), (100, 37, 5, 301), (1000, 24, 990, 34)]:
+        got = host(tks.indexer_scores(tks.Shape(**sh), q, w, k, ks, q0, qn, k0, kn))
+        ref = oracle.index_scores(sh, x["q"], x["w"], x["k"], None, q0, qn, k0, kn)
+        np.testing.assert_array_equal(got.astype(np.float64), ref)
+
+
+def test_tiny_integer_workload_hisa_exact():
+    cfg = CONFIGS[1]
+    say("tiny integer HISA B=64 m=4 + local")
+    x = make_inputs(cfg)
+    sh = cfg.shape_dict()
+    R = cfg.rows
+    rows = np.arange(R)
+    qr, wr = cfg_rows(cfg, x, rows)
+    pooled_o = oracle.pool(sh, x["k"], None, cfg.block)
+    blk_o, bv_o = oracle.block_select(sh, qr, wr, pooled_o, cfg.block, cfg.m_scored, cfg.force, rows)
+    hi_o, hv_o = oracle.refine(sh, qr, wr, x["k"], None, cfg.block, blk_o, cfg.topk, rows)
+    q, w, k, ks = gpu_inputs(x)
+    S = tks.Shape(**sh)
+    pooled = tks.hisa_pool_keys(S, k, ks, cfg.block)
+    blk, bv = tks.hisa_block_select(S, q, w, pooled, cfg.block, cfg.m_scored, cfg.force)
+    idx, vals = tks.hisa_refine_topk(S, q, w, k, ks, cfg.block, blk, cfg.topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(pooled.view(torch.int16)).view(np.uint16), pooled_o)
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    bvg = host(bv).reshape(R, -1).astype(np.float64)
+    np.testing.assert_array_equal(np.isnan(bvg), np.isnan(bv_o))
+    ok = ~np.isnan(bv_o)
+    np.testing.assert_array_equal(bvg[ok], bv_o[ok])
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), hi_o, hv_o, "tiny hisa")
+
+
+# ------------------------------------------------------------------ sweeps
+
+@pytest.mark.parametrize("q_chunk,k_tile", [(0, 0), (256, 1024), (1000, 512), (37, 32),
+                                             (4096, 2048), (3000, 96)])
+def test_chunk_and_tile_sweep_is_exact(q_chunk, k_tile):
+    say("chunk/tile sweep q_chunk=%d k_tile=%d" % (q_chunk, k_tile))
+    sh, x = int_case(20, n_q=3000, n_k=3000, heads=8, dim=64, lo=-3, hi=3)
+    oi, ov = _cached_oracle(("sweep",), sh, x, 256)
+    gi, gv = gpu_flat(sh, x, 256, q_chunk, k_tile)
+    assert_topk_exact(gi, gv, oi, ov, "sweep")
+
+
+_CACHE = {}
+
+
+def _cached_oracle(key, sh, x, topk):
+    key = key + (topk,)
+    if key not in _CACHE:
+        _CACHE[key] = oracle_flat(sh, x, topk)
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("topk", [1, 7, 64, 100, 1024, 2048])
+def test_topk_sweep_is_exact(topk):
+    say("top-k sweep k=%d" % topk)
+    sh, x = int_case(21, n_q=2500, n_k=2500, heads=4, dim=32, lo=-2, hi=2)
+    oi, ov = oracle_flat(sh, x, topk)
+    for qc, kt in [(0, 0), (700, 640)]:
+        gi, gv = gpu_flat(sh, x, topk, qc, kt)
+        assert_topk_exact(gi, gv, oi, ov, "topk=%d qc=%d kt=%d" % (topk, qc, kt))
+
+
+# -------------------------------------------------------------- edge cases
+
+def test_all_equal_scores_take_lowest_indices():
+    say("all-equal scores")
+    sh, x = int_case(22, n_q=300, n_k=300)
+    x["q"] = fp32_to_bf16_bits(np.zeros((1, 300, 4, 32), np.float32))
+    gi, gv = gpu_flat(sh, x, 64)
+    for t in range(300):
+        n = min(64, t + 1)
+        np.testing.assert_array_equal(gi[t, :n], np.arange(n))
+        assert np.all(gi[t, n:] == -1) and np.all(gv[t, :n] == 0) and not np.signbit(gv[t, :n]).any()
+
+
+def test_rows_without_visible_keys_are_padding():
+    say("negative q_pos0: leading rows see no key")
+    sh, x = int_case(23, n_q=64, n_k=64, q_pos0=-5)
+    oi, ov = oracle_flat(sh, x, 16)
+    gi, gv = gpu_flat(sh, x, 16)
+    assert np.all(gi[:5] == -1) and np.all(np.isnan(gv[:5]))
+    assert_topk_exact(gi, gv, oi, ov, "neg pos0")
+
+
+def test_no_keys_at_all():
+    say("n_k = 0")
+    sh, x = int_case(24, n_q=40, n_k=0)
+    x["k"] = np.zeros((1, 0, 32), np.uint16)
+    q, w, _, _ = gpu_inputs(x)
+    k = torch.zeros((1, 0, 32), dtype=torch.bfloat16, device="cuda")
+    idx, vals = tks.topk_flat(tks.Shape(**sh), q, w, k, None, 8)
+    torch.cuda.synchronize()
+    assert np.all(host(idx) == -1)
+
+
+@pytest.mark.parametrize("ratio,q_pos0", [(4, 0), (4, -3), (3, 7)])
+def test_compressed_causality_exact(ratio, q_pos0):
+    say("causal ratio %d q_pos0 %d" % (ratio, q_pos0))
+    sh, x = int_case(25, n_q=1200, n_k=300, ratio=ratio, q_pos0=q_pos0)
+    oi, ov = oracle_flat(sh, x, 50)
+    for qc, kt in [(0, 0), (333, 64)]:
+        gi, gv = gpu_flat(sh, x, 50, qc, kt)
+        assert_topk_exact(gi, gv, oi, ov, "ratio")
+
+
+def test_batched_chunked_prefill_continuation():
+    say("batch 3, 5 new queries at the end of a 700-key cache")
+    sh, x = int_case(26, batch=3, n_q=5, n_k=700, q_pos0=695)
+    oi, ov = oracle_flat(sh, x, 100)
+    for qc, kt in [(0, 0), (4, 160), (1, 32)]:
+        gi, gv = gpu_flat(sh, x, 100, qc, kt)
+        assert_topk_exact(gi, gv, oi, ov, "batch")
+
+
+@pytest.mark.parametrize("heads,dim", [(1, 32), (5, 64), (33, 128), (64, 32), (48, 64), (64, 128)])
+def test_head_and_dim_variants_exact(heads, dim):
+    say("heads %d dim %d" % (heads, dim))
+    sh, x = int_case(27 + heads + dim, n_q=200, n_k=777, heads=heads, dim=dim, q_pos0=577,
+                     lo=-2, hi=2)
+    oi, ov = oracle_flat(sh, x, 128)
+    gi, gv = gpu_flat(sh, x, 128)
+    assert_topk_exact(gi, gv, oi, ov, "heads/dim")
+
+
+def test_fp8_keys_integer_exact():
+    say("fp8 keys, integer codes, power-of-two scales")
+    sh, x = int_case(28, batch=2, n_q=64, n_k=1100, heads=8, dim=128, q_pos0=1036, fp8=True)
+    oi, ov = oracle_flat(sh, x, 200)
+    gi, gv = gpu_flat(sh, x, 200)
+    assert_topk_exact(gi, gv, oi, ov, "fp8")
+
+
+def test_fp8_every_code_decodes_exactly():
+    """One-hot keys: key c holds e4m3fn code c at dim 0, so its score is
+    max(0, q0 * value(c)); compared with torch's e4m3fn decode."""
+    say("fp8 decode of all 256 codes")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    n = len(codes)
+    k8 = np.zeros((1, n, 32), np.uint8)
+    k8[0, :, 0] = codes
+    scale = np.ones((1, n), np.float32)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    for sign in (1.0, -1.0):
+        q = np.zeros((1, 1, 1, 32), np.float32)
+        q[..., 0] = sign
+        sh = dict(batch=1, n_q=1, n_k=n, heads=1, dim=32, q_pos0=n - 1, causal_ratio=1,
+                  key_dtype=KEY_FP8)
+        got = host(tks.indexer_scores(tks.Shape(**sh), dev(fp32_to_bf16_bits(q)),
+                                      dev(np.ones((1, 1, 1), np.float32)), dev(k8), dev(scale),
+                                      0, 1, 0, n))[0, 0]
+        np.testing.assert_array_equal(got.astype(np.float64), np.maximum(sign * ref, 0.0))
+
+
+def test_fp8_pool_bit_exact():
+    say("fp8 pooling vs oracle")
+    cfg = scaled(CONFIGS[4], batch=3, n_k=4096 + 77)
+    from tks_inputs import gen_keys
+    k8, ks = gen_keys(cfg)
+    sh = cfg.shape_dict()
+    for block in (32, 64, 128, 256):
+        ref = oracle.pool(sh, k8, ks, block)
+        got = tks.hisa_pool_keys(tks.Shape(**sh), dev(k8), dev(ks), block)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(got.view(torch.int16)).view(np.uint16), ref)
+
+
+# --------------------------------------------------------------- top-k alone
+
+def brute(scores, n, k):
+    idx = np.arange(n)
+    order = np.lexsort((idx, -scores[:n].astype(np.float64)))
+    out = -np.ones(k, np.int64)
+    out[:min(k, n)] = order[:k]
+    return out
+
+
+@pytest.mark.parametrize("n_cols,topk", [(5000, 2048), (70000, 2048), (300, 64), (1, 1)])
+def test_topk_scores_matches_full_sort(n_cols, topk):
+    say("topk_scores n_cols=%d k=%d" % (n_cols, topk))
+    rng = np.random.default_rng(n_cols)
+    R = 12
+    sc = rng.integers(-20, 20, (R, n_cols)).astype(np.float32)   # heavy ties
+    sc[1] = 0.0
+    sc[2] = -0.0
+    sc[3] = rng.standard_normal(n_cols).astype(np.float32)
+    sc[4, ::2] = -np.inf
+    row_len = rng.integers(0, n_cols + 1, R).astype(np.int32)
+    row_len[0] = n_cols
+    idx, vals = tks.topk_scores(dev(sc), topk, dev(row_len))
+    torch.cuda.synchronize()
+    gi, gv = host(idx), host(vals)
+    for r in range(R):
+        want = brute(sc[r], row_len[r], topk)
+        np.testing.assert_array_equal(gi[r], want, err_msg="row %d" % r)
+        ok = want >= 0
+        np.testing.assert_array_equal(gv[r][ok], sc[r][want[ok]] + np.float32(0.0))
+
+
+# ------------------------------------------------------------------- HISA
+
+def test_hisa_all_blocks_kept_equals_flat():
+    say("HISA with every block kept == flat")
+    sh, x = int_case(29, n_q=1024, n_k=1024, heads=8, dim=64)
+    q, w, k, ks = gpu_inputs(x)
+    S = tks.Shape(**sh)
+    fi, fv = tks.topk_flat(S, q, w, k, ks, 100)
+    for block, flags in ((64, FORCE_LOCAL), (32, FORCE_FIRST | FORCE_LOCAL), (128, FORCE_LOCAL)):
+        hi, hv, blk = tks.hisa_topk(S, q, w, k, ks, block, 1024 // block, flags, 100)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(hi), host(fi))
+        np.testing.assert_array_equal(host(hv), host(fv))
+
+
+def test_hisa_ragged_cache_exact():
+    """n_k not a multiple of the block: the tail block is never pooled or
+    scored, but is refined when it is a query's (forced) local block."""
+    say("HISA ragged cache, batched decode-style rows")
+    sh, x = int_case(30, batch=2, n_q=40, n_k=1000, heads=8, dim=64, q_pos0=960)
+    R = 80
+    rows = np.arange(R)
+    qr = x["q"].reshape(R, 8, 64)
+    wr = x["w"].reshape(R, 8)
+    for block, m, flags in ((64, 3, FORCE_FIRST | FORCE_LOCAL), (128, 2, FORCE_LOCAL),
+                            (32, 0, FORCE_LOCAL), (64, 5, 0)):
+        blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, block, m, flags, 60, rows)
+        q, w, k, ks = gpu_inputs(x)
+        idx, vals, blk = tks.hisa_topk(tks.Shape(**sh), q, w, k, ks, block, m, flags, 60)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+        assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                          "ragged hisa B=%d" % block)
+
+
+def test_small_float_flat_within_tolerance():
+    say("float flat L=2048 H=64 D=128 k=512")
+    cfg = scaled(CONFIGS[2], n_q=2048, n_k=2048, topk=512)
+    x = make_inputs(cfg)
+    sh = cfg.shape_dict()
+    rows = np.arange(0, 2048, 7)
+    qr, wr = cfg_rows(cfg, x, rows)
+    oi, ov = oracle.topk_flat(sh, qr, wr, x["k"], None, cfg.topk, rows)
+    rs = oracle.row_scores(sh, qr, wr, x["k"], None, rows)
+    gi, gv = gpu_flat(sh, x, cfg.topk)
+    rec = check_topk_float(gi[rows], gv[rows], oi, ov, rs, "float flat")
+    print("recall mean %.5f min %.5f" % (rec.mean(), rec.min()))
+    gi2, gv2 = gpu_flat(sh, x, cfg.topk, 300, 512)
+    np.testing.assert_array_equal(gi2, gi)     # tiling does not change a float result
+    np.testing.assert_array_equal(gv2, gv)

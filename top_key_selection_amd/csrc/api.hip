@@ -1,0 +1,515 @@
+// api.hip -- the C ABI of include/tks.h: argument checks, workspace
+// planning and the chunk x tile partition-merge driver (StreamIndex
+// abstract: chunked partition-merge top-k that never materialises the full
+// score tensor).  Every check runs before the first launch; no device
+// memory is allocated here.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/tks.h"
+#include "tks_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(TKS_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxBlkEntries = 512;
+// Score-buffer budget used when a chunk / tile size is left to the library.
+constexpr int64_t kScoreBudget = 256ll << 20;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int check_shape(const tks_shape* s, bool need_keys) {
+    if (!s) return fail(TKS_EINVAL, "shape is NULL");
+    if (s->batch < 0 || s->n_q < 0 || s->n_k < 0)
+        return fail(TKS_EINVAL, "negative size (batch %d, n_q %d, n_k %d)", s->batch, s->n_q, s->n_k);
+    if (s->heads < 1 || s->heads > 64)
+        return fail(TKS_EUNSUPPORTED, "heads = %d (supported 1..64)", s->heads);
+    if (s->dim != 32 && s->dim != 64 && s->dim != 128)
+        return fail(TKS_EUNSUPPORTED, "dim = %d (supported 32, 64, 128)", s->dim);
+    if (s->causal_ratio < 1) return fail(TKS_EINVAL, "causal_ratio = %d (must be >= 1)", s->causal_ratio);
+    if (s->key_dtype != TKS_KEY_BF16 && s->key_dtype != TKS_KEY_FP8_E4M3FN)
+        return fail(TKS_EINVAL, "key_dtype = %d", s->key_dtype);
+    if ((int64_t)s->batch * s->n_q > INT32_MAX || (int64_t)s->batch * s->n_k > INT32_MAX)
+        return fail(TKS_EUNSUPPORTED, "batch * n_q or batch * n_k exceeds 2^31 - 1");
+    (void)need_keys;
+    return TKS_OK;
+}
+
+int check_qwk(const tks_shape* s, const void* q, const float* w, const void* k,
+              const float* k_scale) {
+    const bool rows = (int64_t)s->batch * s->n_q > 0;
+    const bool keys = (int64_t)s->batch * s->n_k > 0;
+    if (rows && (!q || !w)) return fail(TKS_EINVAL, "q or w is NULL");
+    if (keys && !k) return fail(TKS_EINVAL, "k is NULL");
+    if (keys && s->key_dtype == TKS_KEY_FP8_E4M3FN && !k_scale)
+        return fail(TKS_EINVAL, "fp8 keys need k_scale");
+    if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)))
+        return fail(TKS_EINVAL, "q and k must be 16-byte aligned");
+    if ((w && !aligned(w, 4)) || (k_scale && !aligned(k_scale, 4)))
+        return fail(TKS_EINVAL, "w and k_scale must be 4-byte aligned");
+    return TKS_OK;
+}
+
+tks::VisRule vis_tokens(const tks_shape* s) { return tks::VisRule{s->q_pos0, s->causal_ratio, s->n_k, 0}; }
+
+// Largest visible-key count over queries t in [t0, t1] (count is monotone in t).
+int32_t max_visible(const tks_shape* s, int64_t g0, int64_t g1) {
+    // global rows g0..g1-1; if they span a sequence boundary the last query of
+    // a sequence is included
+    const int64_t t_last = (g0 / s->n_q != (g1 - 1) / s->n_q) ? s->n_q - 1 : (g1 - 1) % s->n_q;
+    return vis_tokens(s).tokens((int32_t)t_last);
+}
+
+int block_shift_of(int32_t block) {
+    switch (block) {
+        case 32: return 5;
+        case 64: return 6;
+        case 128: return 7;
+        case 256: return 8;
+        default: return -1;
+    }
+}
+
+// ------------------------------------------------------------- flat planning
+
+struct FlatPlan {
+    int64_t rows;
+    int32_t q_chunk;
+    int32_t k_tile;
+    int64_t score_stride;
+    size_t off_scores, off_run_val, off_run_idx, bytes;
+};
+
+FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile) {
+    FlatPlan p{};
+    p.rows = (int64_t)s->batch * s->n_q;
+    const int32_t maxvis = p.rows > 0 ? max_visible(s, 0, p.rows) : 0;
+    int64_t kt = k_tile > 0 ? k_tile : round_up(std::max<int32_t>(maxvis, 1), 32);
+    int64_t qc;
+    if (q_chunk > 0) {
+        qc = q_chunk;
+    } else {
+        qc = std::max<int64_t>(1, kScoreBudget / (kt * 4));
+        if (k_tile <= 0 && qc < std::min<int64_t>(p.rows, 1024)) {
+            kt = 16384;
+            qc = std::max<int64_t>(1, kScoreBudget / (kt * 4));
+        }
+    }
+    qc = std::max<int64_t>(1, std::min<int64_t>(qc, std::max<int64_t>(p.rows, 1)));
+    p.q_chunk = (int32_t)qc;
+    p.k_tile = (int32_t)kt;
+    p.score_stride = round_up(kt, 4);
+    const bool tiled = kt < maxvis;
+    size_t off = 0;
+    p.off_scores = off;
+    off += round_up(qc * p.score_stride * 4, 256);
+    p.off_run_val = off;
+    if (tiled) off += round_up(qc * (int64_t)topk * 4, 256);
+    p.off_run_idx = off;
+    if (tiled) off += round_up(qc * (int64_t)topk * 4, 256);
+    p.bytes = off;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tks_version(void) { return 100; }
+
+const char* tks_last_error(void) { return g_err; }
+
+int tks_indexer_scores(const tks_shape* s, const void* q, const float* w, const void* k,
+                       const float* k_scale, int32_t q_begin, int32_t q_count, int32_t k_begin,
+                       int32_t k_count, float* scores, hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (q_begin < 0 || q_count < 0 || k_begin < 0 || k_count < 0 ||
+        (int64_t)q_begin + q_count > s->n_q || (int64_t)k_begin + k_count > s->n_k)
+        return fail(TKS_EINVAL, "rectangle [%d,+%d) x [%d,+%d) outside n_q %d / n_k %d", q_begin,
+                    q_count, k_begin, k_count, s->n_q, s->n_k);
+    const int64_t n_rows = (int64_t)s->batch * q_count;
+    if (n_rows == 0 || k_count == 0) return TKS_OK;
+    if ((rc = check_qwk(s, q, w, k, k_scale))) return rc;
+    if (!scores || !aligned(scores, 4)) return fail(TKS_EINVAL, "scores is NULL or misaligned");
+    tks::ScoreArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.w = w;
+    a.k = k;
+    a.k_scale = k_scale;
+    a.k_seq_len = s->n_k;
+    a.heads = s->heads;
+    a.rows = tks::RowMap{0, q_count, q_begin, s->n_q};
+    a.vis = vis_tokens(s);
+    a.col_key0 = k_begin;
+    a.n_cols = k_count;
+    a.out = scores;
+    a.out_stride = k_count;
+    a.write_masked = 1;
+    hipError_t e = tks::launch_score(a, n_rows, s->dim, s->key_dtype == TKS_KEY_FP8_E4M3FN,
+                                     false, stream);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
+    return TKS_OK;
+}
+
+size_t tks_topk_flat_workspace(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile) {
+    if (check_shape(s, true) || topk < 1 || topk > kMaxTopk || q_chunk < 0 || k_tile < 0)
+        return 0;
+    return plan_flat(s, topk, q_chunk, k_tile).bytes;
+}
+
+int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void* k,
+                  const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                  int32_t* idx, float* vals, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (topk < 1 || topk > kMaxTopk)
+        return fail(TKS_EUNSUPPORTED, "topk = %d (supported 1..%d)", topk, kMaxTopk);
+    if (q_chunk < 0 || k_tile < 0) return fail(TKS_EINVAL, "negative q_chunk or k_tile");
+    if (k_tile > 0 && k_tile % 32 != 0)
+        return fail(TKS_EINVAL, "k_tile = %d (must be a multiple of 32)", k_tile);
+    const int64_t rows = (int64_t)s->batch * s->n_q;
+    if (rows == 0) return TKS_OK;
+    if ((rc = check_qwk(s, q, w, k, k_scale))) return rc;
+    if (!idx || !aligned(idx, 4) || (vals && !aligned(vals, 4)))
+        return fail(TKS_EINVAL, "idx is NULL, or idx / vals misaligned");
+    const FlatPlan p = plan_flat(s, topk, q_chunk, k_tile);
+    if (!workspace || workspace_bytes < p.bytes)
+        return fail(TKS_EWORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                    p.bytes);
+    if (!aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
+
+    char* ws = static_cast<char*>(workspace);
+    float* sbuf = reinterpret_cast<float*>(ws + p.off_scores);
+    float* run_val = reinterpret_cast<float*>(ws + p.off_run_val);
+    int32_t* run_idx = reinterpret_cast<int32_t*>(ws + p.off_run_idx);
+    const bool fp8 = s->key_dtype == TKS_KEY_FP8_E4M3FN;
+
+    for (int64_t g0 = 0; g0 < rows; g0 += p.q_chunk) {
+        const int64_t n = std::min<int64_t>(p.q_chunk, rows - g0);
+        const int32_t maxvis = max_visible(s, g0, g0 + n);
+        const int32_t n_tiles = std::max<int32_t>(1, (maxvis + p.k_tile - 1) / p.k_tile);
+        const tks::RowMap rm{g0, s->n_q, 0, s->n_q};
+        for (int32_t ti = 0; ti < n_tiles; ++ti) {
+            const int32_t tb = ti * p.k_tile;
+            const int32_t te = std::min<int32_t>(tb + p.k_tile, maxvis);
+            tks::ScoreArgs a{};
+            a.q = static_cast<const uint16_t*>(q);
+            a.w = w;
+            a.k = k;
+            a.k_scale = k_scale;
+            a.k_seq_len = s->n_k;
+            a.heads = s->heads;
+            a.rows = rm;
+            a.vis = vis_tokens(s);
+            a.col_key0 = tb;
+            a.n_cols = std::max(0, te - tb);
+            a.out = sbuf;
+            a.out_stride = p.score_stride;
+            hipError_t e = tks::launch_score(a, n, s->dim, fp8, false, stream);
+            if (e != hipSuccess) return hip_fail(e, "score launch");
+
+            tks::SelectArgs sa{};
+            sa.scores = sbuf;
+            sa.score_stride = p.score_stride;
+            sa.n_cols = a.n_cols;
+            sa.rows = rm;
+            sa.vis = vis_tokens(s);
+            sa.col_key0 = tb;
+            sa.col_lo = 0;
+            sa.prior_val = n_tiles > 1 ? run_val : nullptr;
+            sa.prior_idx = n_tiles > 1 ? run_idx : nullptr;
+            sa.topk = topk;
+            sa.run_val = run_val;
+            sa.run_idx = run_idx;
+            sa.out_val = vals;
+            sa.out_idx = idx;
+            sa.out_width = topk;
+            sa.tile_begin = tb;
+            sa.tile_end = ti + 1 == n_tiles ? INT32_MAX : te;
+            e = tks::launch_select(sa, n, stream);
+            if (e != hipSuccess) return hip_fail(e, "select launch");
+        }
+    }
+    return TKS_OK;
+}
+
+size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk) {
+    (void)n_rows;
+    (void)n_cols;
+    (void)topk;
+    return 0;
+}
+
+int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,
+                    const int32_t* row_len, int32_t topk, int32_t* idx, float* vals,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (n_rows < 0 || n_cols < 0) return fail(TKS_EINVAL, "negative n_rows / n_cols");
+    if (topk < 1 || topk > kMaxTopk)
+        return fail(TKS_EUNSUPPORTED, "topk = %d (supported 1..%d)", topk, kMaxTopk);
+    if (n_rows == 0) return TKS_OK;
+    if (row_stride < n_cols) return fail(TKS_EINVAL, "row_stride %lld < n_cols %d", (long long)row_stride, n_cols);
+    if ((!scores && n_cols > 0) || !idx) return fail(TKS_EINVAL, "scores or idx is NULL");
+    if ((scores && !aligned(scores, 4)) || !aligned(idx, 4) || (vals && !aligned(vals, 4)) ||
+        (row_len && !aligned(row_len, 4)))
+        return fail(TKS_EINVAL, "misaligned pointer");
+    tks::SelectArgs sa{};
+    sa.scores = scores;
+    sa.score_stride = row_stride;
+    sa.n_cols = n_cols;
+    sa.rows = tks::RowMap{0, n_rows, 0, n_rows};
+    sa.vis = tks::VisRule{INT32_MAX / 2, 1, n_cols, 0};  // every column visible
+    sa.row_len = row_len;
+    sa.topk = topk;
+    sa.out_val = vals;
+    sa.out_idx = idx;
+    sa.out_width = topk;
+    sa.always_final = 1;
+    hipError_t e = tks::launch_select(sa, n_rows, stream);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    return TKS_OK;
+}
+
+int tks_hisa_pool_keys(const tks_shape* s, const void* k, const float* k_scale, int32_t block,
+                       void* pooled, hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (block_shift_of(block) < 0)
+        return fail(TKS_EUNSUPPORTED, "block = %d (supported 32, 64, 128, 256)", block);
+    const int64_t nb = s->n_k / block;
+    if ((int64_t)s->batch * nb == 0) return TKS_OK;
+    if (!k || !aligned(k, 16)) return fail(TKS_EINVAL, "k is NULL or not 16-byte aligned");
+    if (s->key_dtype == TKS_KEY_FP8_E4M3FN && (!k_scale || !aligned(k_scale, 4)))
+        return fail(TKS_EINVAL, "fp8 keys need a 4-byte aligned k_scale");
+    if (!pooled || !aligned(pooled, 16)) return fail(TKS_EINVAL, "pooled is NULL or not 16-byte aligned");
+    tks::PoolArgs a{k, k_scale, s->batch, s->n_k, s->dim, block, static_cast<uint16_t*>(pooled)};
+    hipError_t e = tks::launch_pool(a, s->key_dtype == TKS_KEY_FP8_E4M3FN, stream);
+    if (e != hipSuccess) return hip_fail(e, "pool launch");
+    return TKS_OK;
+}
+
+namespace {
+
+struct BlockPlan {
+    int64_t rows;
+    int32_t nb;
+    int32_t chunk;
+    int64_t stride;
+    size_t bytes;
+};
+
+BlockPlan plan_blocks(const tks_shape* s, int32_t block) {
+    BlockPlan p{};
+    p.rows = (int64_t)s->batch * s->n_q;
+    p.nb = s->n_k / block;
+    p.stride = round_up(std::max<int32_t>(p.nb, 1), 4);
+    p.chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(p.rows, 1),
+                                                               kScoreBudget / (p.stride * 4)));
+    p.bytes = round_up((int64_t)p.chunk * p.stride * 4, 256);
+    return p;
+}
+
+int popcount2(uint32_t f) { return (int)((f & 1u) + ((f >> 1) & 1u)); }
+
+}  // namespace
+
+size_t tks_hisa_block_select_workspace(const tks_shape* s, int32_t block, int32_t m_scored) {
+    if (check_shape(s, true) || block_shift_of(block) < 0 || m_scored < 0) return 0;
+    return plan_blocks(s, block).bytes;
+}
+
+int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, const void* pooled,
+                          int32_t block, int32_t m_scored, uint32_t force_flags, int32_t* blk,
+                          float* blk_vals, int32_t m_total, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (block_shift_of(block) < 0)
+        return fail(TKS_EUNSUPPORTED, "block = %d (supported 32, 64, 128, 256)", block);
+    if (force_flags & ~3u) return fail(TKS_EINVAL, "force_flags = %u", force_flags);
+    if (m_scored < 0 || m_scored > kMaxTopk)
+        return fail(TKS_EUNSUPPORTED, "m_scored = %d (supported 0..%d)", m_scored, kMaxTopk);
+    if (m_total != m_scored + popcount2(force_flags))
+        return fail(TKS_EINVAL, "m_total = %d, expected m_scored + forced = %d", m_total,
+                    m_scored + popcount2(force_flags));
+    if (m_total < 1 || m_total > kMaxBlkEntries)
+        return fail(TKS_EUNSUPPORTED, "m_total = %d (supported 1..%d)", m_total, kMaxBlkEntries);
+    const BlockPlan p = plan_blocks(s, block);
+    if (p.rows == 0) return TKS_OK;
+    if (!q || !w || !aligned(q, 16) || !aligned(w, 4))
+        return fail(TKS_EINVAL, "q / w NULL or misaligned");
+    if (p.nb > 0 && (!pooled || !aligned(pooled, 16)))
+        return fail(TKS_EINVAL, "pooled is NULL or not 16-byte aligned");
+    if (!blk || !aligned(blk, 4) || (blk_vals && !aligned(blk_vals, 4)))
+        return fail(TKS_EINVAL, "blk is NULL, or blk / blk_vals misaligned");
+    if (!workspace || workspace_bytes < p.bytes)
+        return fail(TKS_EWORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                    p.bytes);
+    if (!aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
+
+    float* sbuf = static_cast<float*>(workspace);
+    const tks::VisRule vb{s->q_pos0, s->causal_ratio, s->n_k, block};
+    for (int64_t g0 = 0; g0 < p.rows; g0 += p.chunk) {
+        const int64_t n = std::min<int64_t>(p.chunk, p.rows - g0);
+        const tks::RowMap rm{g0, s->n_q, 0, s->n_q};
+        tks::ScoreArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.w = w;
+        a.k = pooled;
+        a.k_scale = nullptr;
+        a.k_seq_len = p.nb;
+        a.heads = s->heads;
+        a.rows = rm;
+        a.vis = vb;
+        a.col_key0 = 0;
+        a.n_cols = p.nb;
+        a.out = sbuf;
+        a.out_stride = p.stride;
+        hipError_t e = tks::launch_score(a, n, s->dim, false, false, stream);
+        if (e != hipSuccess) return hip_fail(e, "block score launch");
+
+        tks::SelectArgs sa{};
+        sa.scores = sbuf;
+        sa.score_stride = p.stride;
+        sa.n_cols = p.nb;
+        sa.rows = rm;
+        sa.vis = vb;
+        sa.col_key0 = 0;
+        sa.col_lo = (force_flags & TKS_FORCE_FIRST) ? 1 : 0;
+        sa.topk = m_scored;
+        sa.out_val = blk_vals;
+        sa.out_idx = blk;
+        sa.out_width = m_total;
+        sa.always_final = 1;
+        sa.blockselect = 1;
+        sa.force_flags = force_flags;
+        sa.sel_block = block;
+        e = tks::launch_select(sa, n, stream);
+        if (e != hipSuccess) return hip_fail(e, "block select launch");
+    }
+    return TKS_OK;
+}
+
+namespace {
+
+struct RefinePlan {
+    int64_t rows;
+    int32_t slots;
+    int32_t chunk;
+    int64_t stride;
+    size_t bytes;
+};
+
+RefinePlan plan_refine(const tks_shape* s, int32_t block, int32_t m_total, int32_t q_chunk) {
+    RefinePlan p{};
+    p.rows = (int64_t)s->batch * s->n_q;
+    p.slots = block * m_total;
+    p.stride = round_up(p.slots, 4);
+    int64_t c = q_chunk > 0 ? q_chunk : kScoreBudget / (p.stride * 4);
+    p.chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, std::max<int64_t>(p.rows, 1)));
+    p.bytes = round_up((int64_t)p.chunk * p.stride * 4, 256);
+    return p;
+}
+
+}  // namespace
+
+size_t tks_hisa_refine_workspace(const tks_shape* s, int32_t block, int32_t m_total, int32_t topk,
+                                 int32_t q_chunk) {
+    if (check_shape(s, true) || block_shift_of(block) < 0 || m_total < 1 ||
+        m_total > kMaxBlkEntries || topk < 1 || topk > kMaxTopk || q_chunk < 0)
+        return 0;
+    return plan_refine(s, block, m_total, q_chunk).bytes;
+}
+
+int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, const void* k,
+                         const float* k_scale, int32_t block, const int32_t* blk,
+                         int32_t m_total, int32_t topk, int32_t q_chunk, int32_t* idx,
+                         float* vals, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    const int bs = block_shift_of(block);
+    if (bs < 0) return fail(TKS_EUNSUPPORTED, "block = %d (supported 32, 64, 128, 256)", block);
+    if (m_total < 1 || m_total > kMaxBlkEntries)
+        return fail(TKS_EUNSUPPORTED, "m_total = %d (supported 1..%d)", m_total, kMaxBlkEntries);
+    if (topk < 1 || topk > kMaxTopk)
+        return fail(TKS_EUNSUPPORTED, "topk = %d (supported 1..%d)", topk, kMaxTopk);
+    if (q_chunk < 0) return fail(TKS_EINVAL, "negative q_chunk");
+    const RefinePlan p = plan_refine(s, block, m_total, q_chunk);
+    if (p.rows == 0) return TKS_OK;
+    if ((rc = check_qwk(s, q, w, k, k_scale))) return rc;
+    if (!blk || !aligned(blk, 4)) return fail(TKS_EINVAL, "blk is NULL or misaligned");
+    if (!idx || !aligned(idx, 4) || (vals && !aligned(vals, 4)))
+        return fail(TKS_EINVAL, "idx is NULL, or idx / vals misaligned");
+    if (!workspace || workspace_bytes < p.bytes)
+        return fail(TKS_EWORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                    p.bytes);
+    if (!aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
+
+    float* sbuf = static_cast<float*>(workspace);
+    const bool fp8 = s->key_dtype == TKS_KEY_FP8_E4M3FN;
+    for (int64_t g0 = 0; g0 < p.rows; g0 += p.chunk) {
+        const int64_t n = std::min<int64_t>(p.chunk, p.rows - g0);
+        const tks::RowMap rm{g0, s->n_q, 0, s->n_q};
+        tks::ScoreArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.w = w;
+        a.k = k;
+        a.k_scale = k_scale;
+        a.k_seq_len = s->n_k;
+        a.heads = s->heads;
+        a.rows = rm;
+        a.vis = vis_tokens(s);
+        a.n_cols = p.slots;
+        a.blk = blk;
+        a.blk_stride = m_total;
+        a.block_shift = bs;
+        a.out = sbuf;
+        a.out_stride = p.stride;
+        hipError_t e = tks::launch_score(a, n, s->dim, fp8, true, stream);
+        if (e != hipSuccess) return hip_fail(e, "refine score launch");
+
+        tks::SelectArgs sa{};
+        sa.scores = sbuf;
+        sa.score_stride = p.stride;
+        sa.n_cols = p.slots;
+        sa.rows = rm;
+        sa.vis = vis_tokens(s);
+        sa.blk = blk;
+        sa.blk_stride = m_total;
+        sa.block_shift = bs;
+        sa.blocks_mode = 1;
+        sa.topk = topk;
+        sa.out_val = vals;
+        sa.out_idx = idx;
+        sa.out_width = topk;
+        sa.always_final = 1;
+        e = tks::launch_select(sa, n, stream);
+        if (e != hipSuccess) return hip_fail(e, "refine select launch");
+    }
+    return TKS_OK;
+}
+
+}  // extern "C"

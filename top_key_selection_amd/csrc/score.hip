@@ -1,0 +1,248 @@
+// score.hip -- indexer scoring on gfx950 matrix cores.
+//
+// Computes I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]) (HISA abstract:
+// the lightweight token indexer; StreamIndex abstract: H_I indexer heads)
+// for one query row against 32-key sub-blocks:
+//
+//   * the q.k contraction runs on v_mfma_f32_32x32x16_bf16 with the query's
+//     heads as the 32-row M dimension and 32 keys as the N dimension, so one
+//     query's 64 heads are two M blocks and its q fragment (64 x D bf16)
+//     stays in VGPRs for the whole row;
+//   * the 16 k elements one MFMA consumes are split between the two lane
+//     halves: lanes 0-31 take dim [ks*8, ks*8+8), lanes 32-63 take
+//     [D/2 + ks*8, ...), so each lane streams one contiguous D/2 run of a key
+//     row (128 B for bf16, 64 B for fp8) with 16-byte loads;
+//   * the ReLU * w head reduction is fused into the MFMA epilogue: each lane
+//     holds 32 of the 64 heads of one key in its accumulators, reduces them
+//     with FMAs and adds the other half with one lane swap;
+//   * fp8 e4m3fn keys are widened exactly to bf16 in registers
+//     (v_cvt_scalef32_pk_bf16_fp8, scale 1) and the per-token scale is applied
+//     to the reduced score (scale >= 0 commutes with the ReLU).
+#include "tks_launch.hpp"
+
+namespace tks {
+
+namespace {
+
+template <int D, bool FP8>
+struct KeyFrag {
+    // bf16: D/2 bf16 = D bytes per lane; fp8: D/2 bytes per lane.
+    static constexpr int kBytes = FP8 ? D / 2 : D;
+    static constexpr int kVec = kBytes / 16;
+    u32x4 v[kVec];
+};
+
+template <int D, bool FP8>
+__device__ inline void load_key(KeyFrag<D, FP8>& f, const void* k, int64_t row, int hf,
+                                bool valid) {
+    constexpr int KB = KeyFrag<D, FP8>::kBytes;
+    if (valid) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint8_t*>(k) + row * (int64_t)(FP8 ? D : 2 * D) + hf * KB);
+#pragma unroll
+        for (int i = 0; i < KeyFrag<D, FP8>::kVec; ++i) f.v[i] = p[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < KeyFrag<D, FP8>::kVec; ++i) f.v[i] = u32x4{0, 0, 0, 0};
+    }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// B operand of k-step ks from a key fragment.
+template <int D, bool FP8>
+__device__ inline bf16x8 key_operand(const KeyFrag<D, FP8>& f, int ks) {
+    if constexpr (!FP8) {
+        return __builtin_bit_cast(bf16x8, f.v[ks]);
+    } else {
+        // 8 fp8 codes = 2 dwords of vector ks/2
+        const u32x4& v = f.v[ks >> 1];
+        uint32_t d0 = (ks & 1) ? v[2] : v[0];
+        uint32_t d1 = (ks & 1) ? v[3] : v[1];
+        bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, false);
+        bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, true);
+        bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, false);
+        bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, true);
+        bf16x8 r;
+        r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+        r[4] = c[0]; r[5] = c[1]; r[6] = e[0]; r[7] = e[1];
+        return r;
+    }
+}
+
+// WPR (wave per row): each wave owns one row and walks all its slots;
+// otherwise a workgroup owns one row segment and its 4 waves interleave
+// 32-slot sub-blocks.
+template <int D, int MB, bool FP8, bool BLOCKS, bool WPR>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
+                                                    int32_t seg_slots) {
+    constexpr int KS = D / 16;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int hf = lane >> 5;
+
+    const int64_t y = WPR ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+    if (y >= n_rows) return;
+    const int32_t seq = a.rows.seq(y);
+    const int32_t t = a.rows.query(y);
+    const int64_t qr = a.rows.qrow(y);
+    const int32_t n_tok = a.vis.tokens(t);
+
+    int32_t slot_begin, slot_end, step, first;
+    if (WPR) {
+        slot_begin = 0;
+        slot_end = a.n_cols;
+        first = 0;
+        step = 32;
+    } else {
+        slot_begin = blockIdx.y * seg_slots;
+        slot_end = min(a.n_cols, slot_begin + seg_slots);
+        first = wave * 32;
+        step = 128;
+    }
+    // Slots past `limit` are certainly masked.
+    int32_t limit = slot_end;
+    if (!BLOCKS) limit = min(slot_end, max(0, a.vis.count(t) - a.col_key0));
+    const int32_t work_end = a.write_masked ? slot_end : limit;
+    if (slot_begin >= work_end) return;
+
+    // q fragment: A operand rows = heads (mb*32 + m), k elements as above.
+    bf16x8 qa[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int h = mb * 32 + m;
+        if (h < a.heads) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(a.q + (qr * a.heads + h) * D + hf * (D / 2));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, p[ks]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        }
+    }
+    // head weights of this lane's accumulator rows: mb*32 + 8*(j/4) + 4*hf + j%4
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int h = mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
+            wv[mb][j] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+        }
+
+    const int64_t kseq = (int64_t)seq * a.k_seq_len;
+    const int32_t* blk_row = BLOCKS ? a.blk + (a.rows.y0 + y) * a.blk_stride : nullptr;
+    const int32_t bmask = (1 << a.block_shift) - 1;
+
+    auto key_of = [&](int32_t slot, bool& valid) -> int32_t {
+        int32_t key;
+        if (BLOCKS) {
+            // the block list is only read for slots inside the row
+            const int32_t b = slot < limit ? blk_row[slot >> a.block_shift] : -1;
+            // blocks past the last visible key are skipped before the shift
+            const bool ok = b >= 0 && b <= ((n_tok - 1) >> a.block_shift);
+            key = ok ? (b << a.block_shift) + (slot & bmask) : 0;
+            valid = ok && key < n_tok;
+        } else {
+            key = a.col_key0 + slot;
+            valid = slot < limit;
+        }
+        return key;
+    };
+
+    int32_t j0 = slot_begin + first;
+    KeyFrag<D, FP8> cur;
+    bool cvalid;
+    int32_t ckey = key_of(j0 + m, cvalid);
+    load_key<D, FP8>(cur, a.k, kseq + ckey, hf, cvalid && j0 < work_end);
+
+    for (; j0 < work_end; j0 += step) {
+        // prefetch the next sub-block
+        const int32_t j1 = j0 + step;
+        KeyFrag<D, FP8> nxt;
+        bool nvalid;
+        int32_t nkey = key_of(j1 + m, nvalid);
+        load_key<D, FP8>(nxt, a.k, kseq + nkey, hf, nvalid && j1 < work_end);
+        float scale = 1.0f;
+        if (FP8 && cvalid) scale = a.k_scale[kseq + ckey];
+
+        f32x16 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[mb][j] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kb = key_operand<D, FP8>(cur, ks);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s = fmaf(wv[mb][j], fmaxf(acc[mb][j], 0.0f), s);
+        s += __shfl_xor(s, 32);
+        if (FP8) s *= scale;
+        const int32_t slot = j0 + m;
+        if (hf == 0 && slot < slot_end) {
+            if (cvalid)
+                a.out[y * a.out_stride + slot] = s;
+            else if (a.write_masked)
+                a.out[y * a.out_stride + slot] = -__builtin_inff();
+        }
+        cur = nxt;
+        cvalid = nvalid;
+        ckey = nkey;
+    }
+}
+
+template <int D, int MB, bool FP8, bool BLOCKS>
+hipError_t launch_t(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
+    if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
+    if (a.n_cols <= 1024 && !BLOCKS) {
+        dim3 grid((unsigned)((n_rows + 3) / 4));
+        hipLaunchKernelGGL((score_kernel<D, MB, FP8, BLOCKS, true>), grid, dim3(256), 0, stream,
+                           a, n_rows, 0);
+    } else {
+        int32_t seg = 4096;
+        while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
+        dim3 grid((unsigned)n_rows, (unsigned)((a.n_cols + seg - 1) / seg));
+        hipLaunchKernelGGL((score_kernel<D, MB, FP8, BLOCKS, false>), grid, dim3(256), 0, stream,
+                           a, n_rows, seg);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int MB>
+hipError_t launch_d(const ScoreArgs& a, int64_t n_rows, bool fp8, bool blocks, hipStream_t s) {
+    if (fp8)
+        return blocks ? launch_t<D, MB, true, true>(a, n_rows, s)
+                      : launch_t<D, MB, true, false>(a, n_rows, s);
+    return blocks ? launch_t<D, MB, false, true>(a, n_rows, s)
+                  : launch_t<D, MB, false, false>(a, n_rows, s);
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
+                        hipStream_t stream) {
+    const bool two = a.heads > 32;
+    switch (dim) {
+        case 32:
+            return two ? launch_d<32, 2>(a, n_rows, fp8, blocks, stream)
+                       : launch_d<32, 1>(a, n_rows, fp8, blocks, stream);
+        case 64:
+            return two ? launch_d<64, 2>(a, n_rows, fp8, blocks, stream)
+                       : launch_d<64, 1>(a, n_rows, fp8, blocks, stream);
+        case 128:
+            return two ? launch_d<128, 2>(a, n_rows, fp8, blocks, stream)
+                       : launch_d<128, 1>(a, n_rows, fp8, blocks, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tks

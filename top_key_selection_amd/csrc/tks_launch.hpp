@@ -1,0 +1,82 @@
+// tks_launch.hpp -- kernel parameter blocks and host-side launchers of the
+// gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tks_device.hpp"
+
+namespace tks {
+
+// Scoring of one row chunk against a run of key slots (score.hip).
+//   contiguous mode: slot j is key col_key0 + j of the row's sequence;
+//   block mode:      slot j is key blk[row][j / B] * B + j % B.
+// A slot is valid when its key is visible (VisRule) and, in block mode,
+// its block entry is not -1.  Only valid slots are written, unless
+// write_masked is set (then masked slots get -inf).
+struct ScoreArgs {
+    const uint16_t* q;      // bf16 bits [*, n_q, heads, dim]
+    const float* w;         // [*, n_q, heads]
+    const void* k;          // bf16 bits or e4m3fn codes [batch, k_seq_len, dim]
+    const float* k_scale;   // [batch, k_seq_len] (fp8 keys) or null
+    int64_t k_seq_len;      // keys per sequence in `k`
+    int32_t heads;
+    RowMap rows;
+    VisRule vis;
+    int32_t col_key0;
+    int32_t n_cols;
+    const int32_t* blk;     // block mode: kept blocks of global row g at blk + g * blk_stride
+    int32_t blk_stride;
+    int32_t block_shift;
+    float* out;             // chunk-relative rows
+    int64_t out_stride;
+    int32_t write_masked;
+};
+
+// Exact top-k of row candidates (select.hip).  Candidates of a row are the
+// optional prior list (running top-k of earlier key tiles) followed by the
+// valid slots of its score-buffer row, in key-index order.
+struct SelectArgs {
+    const float* scores;
+    int64_t score_stride;
+    int32_t n_cols;
+    RowMap rows;
+    VisRule vis;
+    int32_t col_key0;     // contiguous mode: key of column 0
+    int32_t col_lo;       // contiguous mode: first eligible column
+    const int32_t* row_len;  // explicit valid length per chunk row (overrides vis)
+    const int32_t* blk;   // block mode (as in ScoreArgs)
+    int32_t blk_stride;
+    int32_t block_shift;
+    int32_t blocks_mode;
+    const float* prior_val;   // chunk-relative [n_rows, topk] or null
+    const int32_t* prior_idx;
+    int32_t topk;
+    float* run_val;           // chunk-relative [n_rows, topk]
+    int32_t* run_idx;
+    float* out_val;           // global rows [*, out_width] (may be null)
+    int32_t* out_idx;
+    int32_t out_width;        // topk, or m_total in block-select output mode
+    int32_t tile_begin;       // key range [tile_begin, tile_end) of this pass
+    int32_t tile_end;
+    int32_t always_final;
+    // block-select output mode: kept blocks ascending with forced blocks
+    int32_t blockselect;
+    uint32_t force_flags;
+    int32_t sel_block;        // block size (local block = (tokens - 1) / sel_block)
+};
+
+struct PoolArgs {
+    const void* k;
+    const float* k_scale;
+    int32_t batch, n_k, dim, block;
+    uint16_t* out;
+};
+
+hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
+                        hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream);
+hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
+
+}  // namespace tks

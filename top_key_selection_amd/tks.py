@@ -1,0 +1,273 @@
+"""Python binding of libtks.so (include/tks.h): argument marshalling only.
+
+Every call goes to the HIP library; there is no fallback.  PyTorch provides
+device memory (outputs and workspaces are allocated as torch tensors) and the
+current HIP stream.  Function names mirror the C entry points without the
+``tks_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtks.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+KEY_BF16, KEY_FP8_E4M3FN = 0, 1
+FORCE_FIRST, FORCE_LOCAL = 1, 2
+
+
+class TksError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("tks status %d: %s" % (code, msg))
+        self.code = code
+
+
+class CShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "n_q", "n_k", "heads", "dim", "q_pos0", "causal_ratio", "key_dtype")]
+
+
+@dataclasses.dataclass
+class Shape:
+    batch: int
+    n_q: int
+    n_k: int
+    heads: int
+    dim: int
+    q_pos0: int = 0
+    causal_ratio: int = 1
+    key_dtype: int = KEY_BF16
+
+    def c(self) -> CShape:
+        return CShape(self.batch, self.n_q, self.n_k, self.heads, self.dim, self.q_pos0,
+                      self.causal_ratio, self.key_dtype)
+
+
+SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat_workspace",
+           "tks_topk_flat", "tks_topk_scores_workspace", "tks_topk_scores",
+           "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
+           "tks_hisa_refine_workspace", "tks_hisa_refine_topk")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtks.so; raises if the HIP library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtks.so is not built (run `python -m top_key_selection_amd.build` "
+                          "or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, \
+        ctypes.c_uint32
+    SP = ctypes.POINTER(CShape)
+    L.tks_version.restype = ctypes.c_int
+    L.tks_last_error.restype = ctypes.c_char_p
+    L.tks_indexer_scores.argtypes = [SP, P, P, P, P, i32, i32, i32, i32, P, P]
+    L.tks_topk_flat_workspace.argtypes = [SP, i32, i32, i32]
+    L.tks_topk_flat_workspace.restype = sz
+    L.tks_topk_flat.argtypes = [SP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
+    L.tks_topk_scores_workspace.argtypes = [i32, i32, i32]
+    L.tks_topk_scores_workspace.restype = sz
+    L.tks_topk_scores.argtypes = [P, i32, i32, i64, P, i32, P, P, P, sz, P]
+    L.tks_hisa_pool_keys.argtypes = [SP, P, P, i32, P, P]
+    L.tks_hisa_block_select_workspace.argtypes = [SP, i32, i32]
+    L.tks_hisa_block_select_workspace.restype = sz
+    L.tks_hisa_block_select.argtypes = [SP, P, P, P, i32, i32, u32, P, P, i32, P, sz, P]
+    L.tks_hisa_refine_workspace.argtypes = [SP, i32, i32, i32, i32]
+    L.tks_hisa_refine_workspace.restype = sz
+    L.tks_hisa_refine_topk.argtypes = [SP, P, P, P, P, i32, P, i32, i32, i32, P, P, P, sz, P]
+    for s in L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
+            L.tks_hisa_block_select, L.tks_hisa_refine_topk:
+        s.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().tks_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise TksError(rc, last_error())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtypes):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _key_dtypes(shape: Shape):
+    return _FP8 if shape.key_dtype == KEY_FP8_E4M3FN else _BF16
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A 256-byte aligned device byte buffer (torch's allocator aligns to 512 B)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def version() -> int:
+    return lib().tks_version()
+
+
+def indexer_scores(shape: Shape, q, w, k, k_scale, q_begin, q_count, k_begin, k_count, out=None):
+    """fp32 [batch, q_count, k_count] scores, -inf where not visible."""
+    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
+    _dev(k_scale, "k_scale", (torch.float32,))
+    if out is None:
+        out = torch.empty((shape.batch, q_count, k_count), dtype=torch.float32, device=q.device)
+    S = shape.c()
+    _check(lib().tks_indexer_scores(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), q_begin,
+                                    q_count, k_begin, k_count, _p(out), _stream()))
+    return out
+
+
+def topk_flat_workspace(shape: Shape, topk, q_chunk=0, k_tile=0) -> int:
+    S = shape.c()
+    return int(lib().tks_topk_flat_workspace(ctypes.byref(S), topk, q_chunk, k_tile))
+
+
+def topk_flat(shape: Shape, q, w, k, k_scale, topk, q_chunk=0, k_tile=0, with_vals=True,
+              ws=None, idx=None, vals=None):
+    """Flat indexer top-k: (idx int32 [batch, n_q, topk], vals fp32 | None)."""
+    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
+    _dev(k_scale, "k_scale", (torch.float32,))
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.int32, device=dev)
+    if vals is None and with_vals:
+        vals = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.float32, device=dev)
+    need = topk_flat_workspace(shape, topk, q_chunk, k_tile)
+    if ws is None:
+        ws = workspace(need, dev)
+    S = shape.c()
+    _check(lib().tks_topk_flat(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), topk, q_chunk,
+                               k_tile, _p(idx), _p(vals), _p(ws), ws.numel(), _stream()))
+    return idx, vals
+
+
+def topk_scores(scores, topk, row_len=None, with_vals=True):
+    """Top-k of each row of an fp32 [n_rows, n_cols] (row-strided) score matrix."""
+    _dev(scores, "scores", (torch.float32,)) if scores.is_contiguous() else None
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be 2-D with unit column stride")
+    n_rows, n_cols = scores.shape
+    _dev(row_len, "row_len", (torch.int32,))
+    dev = scores.device
+    idx = torch.empty((n_rows, topk), dtype=torch.int32, device=dev)
+    vals = torch.empty((n_rows, topk), dtype=torch.float32, device=dev) if with_vals else None
+    need = int(lib().tks_topk_scores_workspace(n_rows, n_cols, topk))
+    ws = workspace(need, dev)
+    _check(lib().tks_topk_scores(_p(scores), n_rows, n_cols, scores.stride(0), _p(row_len), topk,
+                                 _p(idx), _p(vals), _p(ws), ws.numel(), _stream()))
+    return idx, vals
+
+
+def hisa_pool_keys(shape: Shape, k, k_scale, block, pooled=None):
+    """bf16 [batch, n_k // block, dim] pooled keys."""
+    _dev(k, "k", _key_dtypes(shape)), _dev(k_scale, "k_scale", (torch.float32,))
+    if pooled is None:
+        pooled = torch.empty((shape.batch, shape.n_k // block, shape.dim), dtype=torch.bfloat16,
+                             device=k.device)
+    S = shape.c()
+    _check(lib().tks_hisa_pool_keys(ctypes.byref(S), _p(k), _p(k_scale), block, _p(pooled),
+                                    _stream()))
+    return pooled
+
+
+def m_total_of(m_scored: int, force_flags: int) -> int:
+    return m_scored + bin(force_flags & 3).count("1")
+
+
+def hisa_block_select_workspace(shape: Shape, block, m_scored) -> int:
+    S = shape.c()
+    return int(lib().tks_hisa_block_select_workspace(ctypes.byref(S), block, m_scored))
+
+
+def hisa_block_select(shape: Shape, q, w, pooled, block, m_scored, force_flags, with_vals=True,
+                      ws=None, blk=None, blk_vals=None):
+    """(blk int32 [batch, n_q, m_total] ascending, blk_vals fp32 | None)."""
+    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(pooled, "pooled", _BF16)
+    m_total = m_total_of(m_scored, force_flags)
+    dev = q.device
+    if blk is None:
+        blk = torch.empty((shape.batch, shape.n_q, m_total), dtype=torch.int32, device=dev)
+    if blk_vals is None and with_vals:
+        blk_vals = torch.empty((shape.batch, shape.n_q, m_total), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(hisa_block_select_workspace(shape, block, m_scored), dev)
+    S = shape.c()
+    _check(lib().tks_hisa_block_select(ctypes.byref(S), _p(q), _p(w), _p(pooled), block, m_scored,
+                                       force_flags, _p(blk), _p(blk_vals), m_total, _p(ws),
+                                       ws.numel(), _stream()))
+    return blk, blk_vals
+
+
+def hisa_refine_workspace(shape: Shape, block, m_total, topk, q_chunk=0) -> int:
+    S = shape.c()
+    return int(lib().tks_hisa_refine_workspace(ctypes.byref(S), block, m_total, topk, q_chunk))
+
+
+def hisa_refine_topk(shape: Shape, q, w, k, k_scale, block, blk, topk, q_chunk=0, with_vals=True,
+                     ws=None, idx=None, vals=None):
+    """(idx int32 [batch, n_q, topk], vals fp32 | None) inside the kept blocks."""
+    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
+    _dev(k_scale, "k_scale", (torch.float32,)), _dev(blk, "blk", (torch.int32,))
+    m_total = blk.shape[-1]
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.int32, device=dev)
+    if vals is None and with_vals:
+        vals = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(hisa_refine_workspace(shape, block, m_total, topk, q_chunk), dev)
+    S = shape.c()
+    _check(lib().tks_hisa_refine_topk(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), block,
+                                      _p(blk), m_total, topk, q_chunk, _p(idx), _p(vals), _p(ws),
+                                      ws.numel(), _stream()))
+    return idx, vals
+
+
+def hisa_topk(shape: Shape, q, w, k, k_scale, block, m_scored, force_flags, topk, pooled=None,
+              with_vals=True):
+    """Whole HISA indexer: pool (unless `pooled` is given), block select, refine.
+    Returns (idx, vals, blk)."""
+    if pooled is None:
+        pooled = hisa_pool_keys(shape, k, k_scale, block)
+    blk, _ = hisa_block_select(shape, q, w, pooled, block, m_scored, force_flags, with_vals=False)
+    idx, vals = hisa_refine_topk(shape, q, w, k, k_scale, block, blk, topk, with_vals=with_vals)
+    return idx, vals, blk
+
+
+def materialized_score_bytes(batch: int, seq: int, heads: int, keys: int) -> int:
+    """Bytes of the [B, S, H_I, T] fp32 score tensor a materialising indexer
+    builds before its top-k (StreamIndex abstract: 256 GB at S = 65,536,
+    H_I = 64, T = S / 4).  This library never allocates it."""
+    return batch * seq * heads * keys * 4
