@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention indexer + top-k hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs
+that are already resident in HBM: the flat (DSA-style) indexer top-k, and the
+HISA indexer (block pooling, block selection, token refinement).  The
+default workload is the 64K-context decode step (64 sequences x 1 query,
+65,536 fp8 e4m3fn keys with per-token scales, 64 heads, dim 128, top-2048;
+HISA blocks of 128 keys, first + local block forced, 62 scored).
+
+Prints one JSON line.  `value` is the number of query-key indexer scores the
+step evaluates per second (flat + HISA block + HISA token scores); the
+per-indexer figures (ms per layer, scores/s, HISA speedup over flat) are in
+"flat" and "hisa".  "roofline" rates the kernel that takes the most time in
+the step, timed with HIP events on its own stream inside the library;
+"cpu_baseline" is the plain CPU oracle timed on a bounded row sample.
+
+    python bench.py [--steps K] [--warmup W] [--config N]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer q-k scores/sec and ms/layer at 64K ctx, flat vs HISA, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload id (4 = 64K decode, the headline; 2, 3, 5 = prefill)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device copy of MIB MiB (rocprofv3 counter calibration)")
+    return ap.parse_args()
+
+
+def workload_desc(cfg):
+    d = dict(workload=cfg.name, batch=cfg.batch, queries=cfg.n_q, keys=cfg.n_k,
+             heads=cfg.heads, dim=cfg.dim, topk=cfg.topk,
+             key_dtype="fp8_e4m3fn+fp32 scale" if cfg.key_dtype else "bf16",
+             q_pos0=cfg.q_pos0, causal_ratio=cfg.causal_ratio)
+    if has_hisa(cfg):
+        d.update(hisa_block=cfg.block, hisa_m_scored=cfg.m_scored,
+                 hisa_forced="first+local" if cfg.force == 3 else "local")
+    if cfg.q_chunk:
+        d.update(q_chunk=cfg.q_chunk, k_tile=cfg.k_tile)
+    return d
+
+
+def has_hisa(cfg):
+    return cfg.dist in ("int", "drift", "fp8")
+
+
+def visible_counts(cfg):
+    import numpy as np
+    t = np.arange(cfg.n_q, dtype=np.int64) + cfg.q_pos0
+    vis = np.floor_divide(t, cfg.causal_ratio)
+    n = np.where(vis < 0, 0, np.minimum(vis + 1, cfg.n_k))
+    return np.tile(n, cfg.batch)
+
+
+def pmc_traffic(role, workload, src_files):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, "pmc_%s_%s.txt" % (role, workload))
+    if not os.path.exists(path):
+        return None
+    info = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            info[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in src_files:
+        h.update(open(os.path.join(ROOT, "top_key_selection_amd", "csrc", f), "rb").read())
+    if info.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(info["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    from tks_inputs import CONFIGS, gen_keys, gen_q, gen_w
+    from top_key_selection_amd import tks
+
+    cfg = CONFIGS[args.config]
+    S = tks.Shape(**cfg.shape_dict())
+    dev = torch.device("cuda:0")
+
+    # ---- inputs resident in HBM
+    k_np, ks_np = gen_keys(cfg)
+    q_np = gen_q(cfg)
+    w_np = gen_w(cfg)
+    q = torch.from_numpy(q_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    del q_np
+    w = torch.from_numpy(w_np).to(dev)
+    k = (torch.from_numpy(k_np).to(dev) if cfg.key_dtype else
+         torch.from_numpy(k_np.view(np.int16)).view(torch.bfloat16).to(dev))
+    ks = torch.from_numpy(ks_np).to(dev) if ks_np is not None else None
+
+    # ---- outputs and workspaces, allocated once
+    R, K = cfg.rows, cfg.topk
+    f_idx = torch.empty((cfg.batch, cfg.n_q, K), dtype=torch.int32, device=dev)
+    f_val = torch.empty_like(f_idx, dtype=torch.float32)
+    f_ws = tks.workspace(tks.topk_flat_workspace(S, K, cfg.q_chunk, cfg.k_tile), dev)
+    hisa = has_hisa(cfg)
+    if hisa:
+        mt = cfg.m_total
+        pooled = torch.empty((cfg.batch, cfg.n_k // cfg.block, cfg.dim), dtype=torch.bfloat16,
+                             device=dev)
+        blk = torch.empty((cfg.batch, cfg.n_q, mt), dtype=torch.int32, device=dev)
+        b_ws = tks.workspace(tks.hisa_block_select_workspace(S, cfg.block, cfg.m_scored), dev)
+        h_idx = torch.empty_like(f_idx)
+        h_val = torch.empty_like(f_val)
+        r_ws = tks.workspace(tks.hisa_refine_workspace(S, cfg.block, mt, K), dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record()
+        tks.topk_flat(S, q, w, k, ks, K, cfg.q_chunk, cfg.k_tile, ws=f_ws, idx=f_idx, vals=f_val)
+        if marks is not None:
+            marks[1].record()
+        if hisa:
+            tks.hisa_pool_keys(S, k, ks, cfg.block, pooled=pooled)
+            if marks is not None:
+                marks[2].record()
+            tks.hisa_block_select(S, q, w, pooled, cfg.block, cfg.m_scored, cfg.force,
+                                  with_vals=False, ws=b_ws, blk=blk)
+            tks.hisa_refine_topk(S, q, w, k, ks, cfg.block, blk, K, ws=r_ws, idx=h_idx,
+                                 vals=h_val)
+            if marks is not None:
+                marks[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events between the calls
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_step = wall_s * 1e3 / args.steps
+    flat_ms = float(np.median([m[0].elapsed_time(m[1]) for m in marks]))
+    if hisa:
+        pool_ms = float(np.median([m[1].elapsed_time(m[2]) for m in marks]))
+        hisa_ms = float(np.median([m[2].elapsed_time(m[3]) for m in marks]))
+
+    # ---- per-kernel times: the same steps again with library event brackets
+    tks.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    roles = {}
+    for role in tks.PROFILE_ROLES:
+        tot, n = tks.profile_read(role)
+        if n:
+            roles[role] = (tot, n)
+    tks.profile_enable(False)
+
+    # ---- work counts
+    nvis = visible_counts(cfg)
+    flat_pairs = int(nvis.sum())
+    out = {}
+    if hisa:
+        blk_np = blk.cpu().numpy().reshape(R, -1)
+        L = np.where(nvis > 0, (nvis - 1) // cfg.block, -1)
+        block_pairs = int(np.maximum(L, 0).sum())           # pooled blocks scored per row
+        tok = 0
+        for r in range(R):
+            kept = blk_np[r][blk_np[r] >= 0]
+            tok += int(np.minimum(np.maximum(nvis[r] - kept * cfg.block, 0), cfg.block).sum())
+        hisa_pairs = block_pairs + tok
+        fi = f_idx.cpu().numpy().reshape(R, -1)
+        hi = h_idx.cpu().numpy().reshape(R, -1)
+        ious = []
+        for r in range(0, R, max(1, R // 256)):
+            a, b = set(fi[r][fi[r] >= 0].tolist()), set(hi[r][hi[r] >= 0].tolist())
+            ious.append(len(a & b) / max(1, len(a | b)))
+        out["hisa"] = dict(
+            ms_per_layer=round(hisa_ms, 4),
+            ms_per_layer_with_pool=round(hisa_ms + pool_ms, 4),
+            pool_ms=round(pool_ms, 4),
+            qk_scores_scored=hisa_pairs,
+            qk_scores_per_s_scored=hisa_pairs / (hisa_ms * 1e-3),
+            qk_scores_per_s_flat_equivalent=flat_pairs / (hisa_ms * 1e-3),
+            speedup_vs_flat=round(flat_ms / hisa_ms, 3),
+            speedup_vs_flat_with_pool=round(flat_ms / (hisa_ms + pool_ms), 3),
+            iou_vs_flat_mean=round(float(np.mean(ious)), 4))
+    else:
+        hisa_pairs = 0
+    out["flat"] = dict(ms_per_layer=round(flat_ms, 4), qk_scores=flat_pairs,
+                       qk_scores_per_s=flat_pairs / (flat_ms * 1e-3))
+    total_pairs = flat_pairs + hisa_pairs
+    value = total_pairs / (ms_step * 1e-3)
+
+    # ---- roofline of the dominant kernel
+    kb = cfg.dim * (1 if cfg.key_dtype else 2) + (4 if cfg.key_dtype else 0)
+    flops_pair = 2 * cfg.heads * cfg.dim
+    qw = cfg.heads * (cfg.dim * 2 + 4)
+    algo = {}
+    if "score_flat" in roles:
+        n_launch = roles["score_flat"][1] / args.steps
+        shared = cfg.n_q > 1        # prefill: keys shared by the query rows
+        bytes_ = flat_pairs * 4 + R * qw + (cfg.batch * cfg.n_k * kb if shared else flat_pairs * kb)
+        algo["score_flat"] = (bytes_ / n_launch, flat_pairs * flops_pair / n_launch)
+    if "pool" in roles:
+        nb = cfg.n_k // cfg.block
+        bytes_ = cfg.batch * nb * cfg.block * kb + cfg.batch * nb * cfg.dim * 2
+        algo["pool"] = (bytes_, 0.0)
+    if "score_refine" in roles and hisa:
+        n_launch = roles["score_refine"][1] / args.steps
+        algo["score_refine"] = ((tok * (kb + 4) + R * qw) / n_launch, tok * flops_pair / n_launch)
+    if "score_pooled" in roles and hisa:
+        n_launch = roles["score_pooled"][1] / args.steps
+        algo["score_pooled"] = ((block_pairs * 4 + R * qw + cfg.batch * (cfg.n_k // cfg.block) *
+                                 cfg.dim * 2) / n_launch, block_pairs * flops_pair / n_launch)
+    dom = max(roles, key=lambda r: roles[r][0])
+    tot, n = roles[dom]
+    avg_ms = tot / n
+    roof = None
+    if dom in algo:
+        b, f = algo[dom]
+        ai = f / b if b else 0.0
+        if ai > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            ach = f / (avg_ms * 1e-3) / 1e12
+            roof = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
+        else:
+            ach = b / (avg_ms * 1e-3) / 1e9
+            roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(ach / HBM_PEAK_GBS, 4))
+        roof.update(kernel=dom, avg_launch_ms=round(avg_ms, 5),
+                    algorithmic_bytes_per_launch=int(b), algorithmic_flops_per_launch=int(f))
+        src = {"score_flat": ["score.hip"], "score_refine": ["score.hip"],
+               "score_pooled": ["score.hip"], "pool": ["pool.hip"], "select": ["select.hip"]}[dom]
+        roof["traffic"] = pmc_traffic(dom, cfg.name, src)
+    kern = {r: dict(avg_ms=round(t / n, 5), launches_per_step=n / args.steps)
+            for r, (t, n) in roles.items()}
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, k_np, ks_np, nvis, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "q-k scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": workload_desc(cfg),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        **out,
+        "kernels": kern,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, k_np, ks_np, nvis, target_s):
+    """The CPU oracle, as it stands, on a sample of the workload's rows: flat
+    top-k and (where the workload has it) HISA pooling / selection /
+    refinement of those rows.  Rate in q-k scores per second."""
+    import numpy as np
+
+    import oracle
+    from tks_inputs import gen_q_rows, gen_w_rows
+
+    threads = oracle.num_threads()
+    R = cfg.rows
+    # pick rows from the end (the longest) and grow the sample until the
+    # estimated time reaches the target
+    order = np.argsort(-nvis, kind="stable")
+    probe = order[:1]
+    t0 = time.perf_counter()
+    sh = cfg.shape_dict()
+    oracle.topk_flat(sh, gen_q_rows(cfg, probe), gen_w_rows(cfg, probe), k_np, ks_np, cfg.topk,
+                     probe, with_vals=False)
+    per_row = max(time.perf_counter() - t0, 1e-4)
+    # rows run in parallel, one per thread; HISA roughly doubles the per-row cost
+    n = int(target_s * threads / (per_row * (2 if has_hisa(cfg) else 1)))
+    n = max(1, min(R, n))
+    rows = np.sort(order[:n])
+    qr, wr = gen_q_rows(cfg, rows), gen_w_rows(cfg, rows)
+    pairs = int(nvis[rows].sum())
+    t0 = time.perf_counter()
+    oracle.topk_flat(sh, qr, wr, k_np, ks_np, cfg.topk, rows, with_vals=False)
+    if has_hisa(cfg):
+        seqs = np.unique(rows // cfg.n_q)
+        sub = dict(sh, batch=len(seqs))
+        kk = k_np[seqs]
+        kks = ks_np[seqs] if ks_np is not None else None
+        remap = {int(s): i for i, s in enumerate(seqs)}
+        lrows = np.array([remap[int(r) // cfg.n_q] * cfg.n_q + int(r) % cfg.n_q for r in rows])
+        blk, _, _ = oracle.hisa(sub, qr, wr, kk, kks, cfg.block, cfg.m_scored, cfg.force,
+                                cfg.topk, lrows, with_vals=False)
+        L = np.where(nvis[rows] > 0, (nvis[rows] - 1) // cfg.block, -1)
+        pairs += int(np.maximum(L, 0).sum())
+        for i in range(len(rows)):
+            kept = blk[i][blk[i] >= 0]
+            pairs += int(np.minimum(np.maximum(nvis[rows[i]] - kept * cfg.block, 0),
+                                    cfg.block).sum())
+    dt = time.perf_counter() - t0
+    what = "flat top-k" + (" + HISA (pooling of the sampled sequences, block select, refine)"
+                           if has_hisa(cfg) else "")
+    return dict(value=pairs / dt, unit="q-k scores/s", cores=threads, kind="oracle",
+                seconds=round(dt, 2),
+                sample="%d of %d query rows (the longest), %s, %d q-k scores" % (
+                    len(rows), R, what, pairs))
+
+
+if __name__ == "__main__":
+    main()

@@ -175,6 +175,22 @@ int tks_hisa_refine_topk(const tks_shape* shape, const void* q, const float* w, 
                          float* vals, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * Kernel timing instrumentation (for benchmarks and profiling).  While
+ * enabled, every kernel launch the library makes is bracketed by a pair of
+ * HIP events recorded on the launch's stream.  tks_profile_enable(1) clears
+ * earlier records.  tks_profile_read() waits for the recorded events and
+ * returns the summed duration and launch count of one kernel role:
+ *   "score_flat"   -- token scoring of tks_topk_flat / tks_indexer_scores
+ *   "score_pooled" -- pooled-block scoring of tks_hisa_block_select
+ *   "score_refine" -- gathered-block scoring of tks_hisa_refine_topk
+ *   "select"       -- every top-k selection launch
+ *   "pool"         -- tks_hisa_pool_keys
+ * Returns TKS_EINVAL for an unknown role or NULL outputs.
+ */
+int tks_profile_enable(int on);
+int tks_profile_read(const char* role, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

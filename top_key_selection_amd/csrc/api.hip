@@ -8,6 +8,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "../../include/tks.h"
 #include "tks_launch.hpp"
@@ -26,6 +29,47 @@ int fail(int code, const char* fmt, ...) {
 
 int hip_fail(hipError_t e, const char* where) {
     return fail(TKS_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------- instrumentation
+
+struct TimedLaunch {
+    std::string role;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<TimedLaunch> g_prof;
+
+// Brackets one launch with events on its stream while profiling is enabled.
+class Timed {
+  public:
+    Timed(const char* role, hipStream_t s) : s_(s) {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        if (!g_prof_on) return;
+        on_ = hipEventCreate(&rec_.start) == hipSuccess && hipEventCreate(&rec_.stop) == hipSuccess &&
+              hipEventRecord(rec_.start, s_) == hipSuccess;
+        rec_.role = role;
+    }
+    ~Timed() {
+        if (!on_) return;
+        if (hipEventRecord(rec_.stop, s_) != hipSuccess) return;
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        g_prof.push_back(rec_);
+    }
+
+  private:
+    hipStream_t s_;
+    bool on_ = false;
+    TimedLaunch rec_;
+};
+
+void prof_clear() {
+    for (auto& r : g_prof) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
 }
 
 constexpr int kMaxTopk = 2048;
@@ -165,8 +209,12 @@ int tks_indexer_scores(const tks_shape* s, const void* q, const float* w, const 
     a.out = scores;
     a.out_stride = k_count;
     a.write_masked = 1;
-    hipError_t e = tks::launch_score(a, n_rows, s->dim, s->key_dtype == TKS_KEY_FP8_E4M3FN,
-                                     false, stream);
+    hipError_t e;
+    {
+        Timed tm("score_flat", stream);
+        e = tks::launch_score(a, n_rows, s->dim, s->key_dtype == TKS_KEY_FP8_E4M3FN, false,
+                              stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "score launch");
     return TKS_OK;
 }
@@ -226,7 +274,11 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
             a.n_cols = std::max(0, te - tb);
             a.out = sbuf;
             a.out_stride = p.score_stride;
-            hipError_t e = tks::launch_score(a, n, s->dim, fp8, false, stream);
+            hipError_t e;
+            {
+                Timed tm("score_flat", stream);
+                e = tks::launch_score(a, n, s->dim, fp8, false, stream);
+            }
             if (e != hipSuccess) return hip_fail(e, "score launch");
 
             tks::SelectArgs sa{};
@@ -247,7 +299,10 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
             sa.out_width = topk;
             sa.tile_begin = tb;
             sa.tile_end = ti + 1 == n_tiles ? INT32_MAX : te;
-            e = tks::launch_select(sa, n, stream);
+            {
+                Timed tm("select", stream);
+                e = tks::launch_select(sa, n, stream);
+            }
             if (e != hipSuccess) return hip_fail(e, "select launch");
         }
     }
@@ -287,7 +342,11 @@ int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t
     sa.out_idx = idx;
     sa.out_width = topk;
     sa.always_final = 1;
-    hipError_t e = tks::launch_select(sa, n_rows, stream);
+    hipError_t e;
+    {
+        Timed tm("select", stream);
+        e = tks::launch_select(sa, n_rows, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "select launch");
     return TKS_OK;
 }
@@ -305,7 +364,11 @@ int tks_hisa_pool_keys(const tks_shape* s, const void* k, const float* k_scale, 
         return fail(TKS_EINVAL, "fp8 keys need a 4-byte aligned k_scale");
     if (!pooled || !aligned(pooled, 16)) return fail(TKS_EINVAL, "pooled is NULL or not 16-byte aligned");
     tks::PoolArgs a{k, k_scale, s->batch, s->n_k, s->dim, block, static_cast<uint16_t*>(pooled)};
-    hipError_t e = tks::launch_pool(a, s->key_dtype == TKS_KEY_FP8_E4M3FN, stream);
+    hipError_t e;
+    {
+        Timed tm("pool", stream);
+        e = tks::launch_pool(a, s->key_dtype == TKS_KEY_FP8_E4M3FN, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "pool launch");
     return TKS_OK;
 }
@@ -387,7 +450,11 @@ int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, con
         a.n_cols = p.nb;
         a.out = sbuf;
         a.out_stride = p.stride;
-        hipError_t e = tks::launch_score(a, n, s->dim, false, false, stream);
+        hipError_t e;
+        {
+            Timed tm("score_pooled", stream);
+            e = tks::launch_score(a, n, s->dim, false, false, stream);
+        }
         if (e != hipSuccess) return hip_fail(e, "block score launch");
 
         tks::SelectArgs sa{};
@@ -406,7 +473,10 @@ int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, con
         sa.blockselect = 1;
         sa.force_flags = force_flags;
         sa.sel_block = block;
-        e = tks::launch_select(sa, n, stream);
+        {
+            Timed tm("select", stream);
+            e = tks::launch_select(sa, n, stream);
+        }
         if (e != hipSuccess) return hip_fail(e, "block select launch");
     }
     return TKS_OK;
@@ -488,7 +558,11 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
         a.block_shift = bs;
         a.out = sbuf;
         a.out_stride = p.stride;
-        hipError_t e = tks::launch_score(a, n, s->dim, fp8, true, stream);
+        hipError_t e;
+        {
+            Timed tm("score_refine", stream);
+            e = tks::launch_score(a, n, s->dim, fp8, true, stream);
+        }
         if (e != hipSuccess) return hip_fail(e, "refine score launch");
 
         tks::SelectArgs sa{};
@@ -506,9 +580,43 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
         sa.out_idx = idx;
         sa.out_width = topk;
         sa.always_final = 1;
-        e = tks::launch_select(sa, n, stream);
+        {
+            Timed tm("select", stream);
+            e = tks::launch_select(sa, n, stream);
+        }
         if (e != hipSuccess) return hip_fail(e, "refine select launch");
     }
+    return TKS_OK;
+}
+
+int tks_profile_enable(int on) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (on) prof_clear();
+    g_prof_on = on != 0;
+    return TKS_OK;
+}
+
+int tks_profile_read(const char* role, double* total_ms, int64_t* launches) {
+    static const char* kRoles[] = {"score_flat", "score_pooled", "score_refine", "select", "pool"};
+    if (!role || !total_ms || !launches) return fail(TKS_EINVAL, "NULL argument");
+    bool known = false;
+    for (const char* r : kRoles) known = known || strcmp(r, role) == 0;
+    if (!known) return fail(TKS_EINVAL, "unknown kernel role '%s'", role);
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    double sum = 0.0;
+    int64_t n = 0;
+    for (auto& r : g_prof) {
+        if (r.role != role) continue;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "profile event");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "profile event");
+        sum += ms;
+        ++n;
+    }
+    *total_ms = sum;
+    *launches = n;
     return TKS_OK;
 }
 

@@ -51,7 +51,8 @@ class Shape:
 SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat_workspace",
            "tks_topk_flat", "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
-           "tks_hisa_refine_workspace", "tks_hisa_refine_topk")
+           "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_profile_enable",
+           "tks_profile_read")
 
 _lib = None
 
@@ -84,7 +85,9 @@ def lib() -> ctypes.CDLL:
     L.tks_hisa_refine_workspace.argtypes = [SP, i32, i32, i32, i32]
     L.tks_hisa_refine_workspace.restype = sz
     L.tks_hisa_refine_topk.argtypes = [SP, P, P, P, P, i32, P, i32, i32, i32, P, P, P, sz, P]
-    for s in L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
+    L.tks_profile_enable.argtypes = [ctypes.c_int]
+    L.tks_profile_read.argtypes = [ctypes.c_char_p, P, P]
+    for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
             L.tks_hisa_block_select, L.tks_hisa_refine_topk:
         s.restype = ctypes.c_int
     _lib = L
@@ -264,6 +267,22 @@ def hisa_topk(shape: Shape, q, w, k, k_scale, block, m_scored, force_flags, topk
     blk, _ = hisa_block_select(shape, q, w, pooled, block, m_scored, force_flags, with_vals=False)
     idx, vals = hisa_refine_topk(shape, q, w, k, k_scale, block, blk, topk, with_vals=with_vals)
     return idx, vals, blk
+
+
+PROFILE_ROLES = ("score_flat", "score_pooled", "score_refine", "select", "pool")
+
+
+def profile_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events (see tks.h)."""
+    _check(lib().tks_profile_enable(1 if on else 0))
+
+
+def profile_read(role: str):
+    """(total_ms, launches) of one kernel role since profile_enable(True)."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().tks_profile_read(role.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def materialized_score_bytes(batch: int, seq: int, heads: int, keys: int) -> int:
