@@ -121,6 +121,8 @@ int tks_topk_flat(const tks_shape* shape, const void* q, const float* w, const v
  * scores + r * row_stride (row_len NULL: n_cols for every row); candidate j
  * of a row is key index j.  Scores must not be NaN.
  *   idx / vals: [n_rows, topk] (vals may be NULL).
+ *   workspace: tks_topk_scores_workspace(n_rows, n_cols, topk) bytes (currently
+ *   0 for every size; NULL is then accepted).
  */
 size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk);
 int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,

@@ -319,8 +319,6 @@ size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk) {
 int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,
                     const int32_t* row_len, int32_t topk, int32_t* idx, float* vals,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (n_rows < 0 || n_cols < 0) return fail(TKS_EINVAL, "negative n_rows / n_cols");
     if (topk < 1 || topk > kMaxTopk)
         return fail(TKS_EUNSUPPORTED, "topk = %d (supported 1..%d)", topk, kMaxTopk);
@@ -342,6 +340,8 @@ int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t
     sa.out_idx = idx;
     sa.out_width = topk;
     sa.always_final = 1;
+    (void)workspace;
+    (void)workspace_bytes;
     hipError_t e;
     {
         Timed tm("select", stream);

@@ -40,20 +40,21 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a, int64_t n_threads
     if (FP8) {
         const uint8_t* base = reinterpret_cast<const uint8_t*>(a.k) + s0 * a.dim + d0;
         const float* sc = a.k_scale + s0;
-#pragma unroll 8
+#pragma unroll 16
         for (int s = 0; s < a.block; ++s) {
             const uint32_t c = *reinterpret_cast<const uint32_t*>(base + (int64_t)s * a.dim);
             const double scale = (double)sc[s];
             const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
             const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
-            acc0 += scale * (double)lo[0];
-            acc1 += scale * (double)lo[1];
-            acc2 += scale * (double)hi[0];
-            acc3 += scale * (double)hi[1];
+            // scale * code is exact in fp64, so one fused rounding = add
+            acc0 = fma(scale, (double)lo[0], acc0);
+            acc1 = fma(scale, (double)lo[1], acc1);
+            acc2 = fma(scale, (double)hi[0], acc2);
+            acc3 = fma(scale, (double)hi[1], acc3);
         }
     } else {
         const uint16_t* base = reinterpret_cast<const uint16_t*>(a.k) + s0 * a.dim + d0;
-#pragma unroll 8
+#pragma unroll 16
         for (int s = 0; s < a.block; ++s) {
             const u32x2 v = *reinterpret_cast<const u32x2*>(base + (int64_t)s * a.dim);
             acc0 += (double)__uint_as_float(v[0] << 16);

@@ -18,6 +18,8 @@
 //   * fp8 e4m3fn keys are widened exactly to bf16 in registers
 //     (v_cvt_scalef32_pk_bf16_fp8, scale 1) and the per-token scale is applied
 //     to the reduced score (scale >= 0 commutes with the ReLU).
+#include <algorithm>
+
 #include "tks_launch.hpp"
 
 namespace tks {
@@ -32,19 +34,16 @@ struct KeyFrag {
     u32x4 v[kVec];
 };
 
+// Branch-free fragment load (the caller clamps `row` into the key tensor for
+// slots that hold no key), so the compiler can keep several loads in
+// flight and wait for each one by count.
 template <int D, bool FP8>
-__device__ inline void load_key(KeyFrag<D, FP8>& f, const void* k, int64_t row, int hf,
-                                bool valid) {
+__device__ inline void load_key(KeyFrag<D, FP8>& f, const void* k, int64_t row, int hf) {
     constexpr int KB = KeyFrag<D, FP8>::kBytes;
-    if (valid) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const uint8_t*>(k) + row * (int64_t)(FP8 ? D : 2 * D) + hf * KB);
+    const u32x4* p = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(k) + row * (int64_t)(FP8 ? D : 2 * D) + hf * KB);
 #pragma unroll
-        for (int i = 0; i < KeyFrag<D, FP8>::kVec; ++i) f.v[i] = p[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < KeyFrag<D, FP8>::kVec; ++i) f.v[i] = u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < KeyFrag<D, FP8>::kVec; ++i) f.v[i] = p[i];
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -151,67 +150,97 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
         return key;
     };
 
-    int32_t j0 = slot_begin + first;
-    KeyFrag<D, FP8> cur;
-    bool cvalid;
-    int32_t ckey = key_of(j0 + m, cvalid);
-    load_key<D, FP8>(cur, a.k, kseq + ckey, hf, cvalid && j0 < work_end);
-
-    for (; j0 < work_end; j0 += step) {
-        // prefetch the next sub-block
-        const int32_t j1 = j0 + step;
-        KeyFrag<D, FP8> nxt;
-        bool nvalid;
-        int32_t nkey = key_of(j1 + m, nvalid);
-        load_key<D, FP8>(nxt, a.k, kseq + nkey, hf, nvalid && j1 < work_end);
-        float scale = 1.0f;
-        if (FP8 && cvalid) scale = a.k_scale[kseq + ckey];
-
+    // One 32-slot sub-block: MFMA over the key fragment, fused ReLU * w head
+    // reduction, store.  `scale` is the key's fp8 scale (1 for bf16).
+    auto process = [&](const KeyFrag<D, FP8>& f, int32_t j, bool valid, float scale) {
         f32x16 acc[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[mb][j] = 0.0f;
+            for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kb = key_operand<D, FP8>(cur, ks);
+            const bf16x8 kb = key_operand<D, FP8>(f, ks);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
         }
-        float s = 0.0f;
+        float sc = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s = fmaf(wv[mb][j], fmaxf(acc[mb][j], 0.0f), s);
-        s += __shfl_xor(s, 32);
-        if (FP8) s *= scale;
-        const int32_t slot = j0 + m;
+            for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], fmaxf(acc[mb][i], 0.0f), sc);
+        sc += __shfl_xor(sc, 32);
+        if (FP8) sc *= scale;
+        const int32_t slot = j + m;
         if (hf == 0 && slot < slot_end) {
-            if (cvalid)
-                a.out[y * a.out_stride + slot] = s;
+            if (valid)
+                a.out[y * a.out_stride + slot] = sc;
             else if (a.write_masked)
                 a.out[y * a.out_stride + slot] = -__builtin_inff();
         }
-        cur = nxt;
-        cvalid = nvalid;
-        ckey = nkey;
+    };
+    // Fetch the fragment (and fp8 scale) of this lane's key of sub-block j;
+    // slots without a key read key 0 of the sequence and are never stored.
+    auto fetch = [&](KeyFrag<D, FP8>& f, int32_t j, bool& valid, float& scale) {
+        const int32_t key = key_of(j + m, valid);
+        valid = valid && j < work_end;
+        const int64_t row = kseq + (valid ? key : 0);
+        load_key<D, FP8>(f, a.k, row, hf);
+        if (FP8) scale = a.k_scale[row];
+    };
+
+    // Ring of fragments in flight, unrolled so that no register is rotated
+    // and the loop body has no early exit: a sub-block past the end is
+    // computed on a clamped address and never stored.
+    int32_t j0 = slot_begin + first;
+    if constexpr (FP8) {
+        // fp8 fragments are 16 VGPRs: three sub-blocks in flight
+        KeyFrag<D, FP8> f0, f1, f2;
+        bool v0, v1, v2;
+        float s0 = 1.0f, s1 = 1.0f, s2 = 1.0f;
+        fetch(f0, j0, v0, s0);
+        fetch(f1, j0 + step, v1, s1);
+        fetch(f2, j0 + 2 * step, v2, s2);
+        for (; j0 < work_end; j0 += 3 * step) {
+            process(f0, j0, v0, s0);
+            fetch(f0, j0 + 3 * step, v0, s0);
+            process(f1, j0 + step, v1, s1);
+            fetch(f1, j0 + 4 * step, v1, s1);
+            process(f2, j0 + 2 * step, v2, s2);
+            fetch(f2, j0 + 5 * step, v2, s2);
+        }
+    } else {
+        KeyFrag<D, FP8> f0, f1;
+        bool v0, v1;
+        float s0 = 1.0f, s1 = 1.0f;
+        fetch(f0, j0, v0, s0);
+        fetch(f1, j0 + step, v1, s1);
+        for (; j0 < work_end; j0 += 2 * step) {
+            process(f0, j0, v0, s0);
+            fetch(f0, j0 + 2 * step, v0, s0);
+            process(f1, j0 + step, v1, s1);
+            fetch(f1, j0 + 3 * step, v1, s1);
+        }
     }
 }
 
 template <int D, int MB, bool FP8, bool BLOCKS>
 hipError_t launch_t(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
-    if (a.n_cols <= 1024 && !BLOCKS) {
+    if (a.n_cols <= 1024 && !BLOCKS && n_rows >= 8192) {
+        // many short rows: one wave per row
         dim3 grid((unsigned)((n_rows + 3) / 4));
         hipLaunchKernelGGL((score_kernel<D, MB, FP8, BLOCKS, true>), grid, dim3(256), 0, stream,
                            a, n_rows, 0);
     } else {
-        int32_t seg = 4096;
+        // a workgroup per row segment; segments sized for >= ~2048 workgroups
+        const int64_t want = (n_rows * (int64_t)a.n_cols + 2047) / 2048;
+        int64_t seg = std::min<int64_t>(4096, std::max<int64_t>(128, (want + 127) / 128 * 128));
         while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
         dim3 grid((unsigned)n_rows, (unsigned)((a.n_cols + seg - 1) / seg));
         hipLaunchKernelGGL((score_kernel<D, MB, FP8, BLOCKS, false>), grid, dim3(256), 0, stream,
-                           a, n_rows, seg);
+                           a, n_rows, (int32_t)seg);
     }
     return hipGetLastError();
 }

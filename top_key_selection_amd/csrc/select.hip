@@ -1,292 +1,280 @@
-// select.hip -- exact per-query top-k on gfx950 (one workgroup per row).
+// select.hip -- exact per-query top-k on gfx950.
 //
 // The per-query top-k of the HISA abstract (a per-query set of k token
 // indices) and the partition-merge of the StreamIndex abstract (a partial
 // top-k per key tile merged into a running list) both reduce to one
 // operation: from a row's candidates -- the running list of earlier tiles
-// followed by this tile's scores, in key-index order -- keep the k best in
-// the total order (score descending, key index ascending).
+// plus this tile's scores -- keep the k best in the total order (score
+// descending, key index ascending).
 //
-//   1. Radix select on the orderable 32-bit key of each score, 8 bits per
-//      pass from the top, finds the k-th key's bucket; per-wave LDS
-//      histograms keep atomic contention inside a wave.  A pass that finds a
-//      bucket whose entries are all needed stops early.
-//   2. One ordered pass collects every candidate above the bucket (atomic
-//      append) and the first `need` candidates inside it in key-index order
-//      (a workgroup prefix count), which is exactly the tie rule.
-//   3. A bitonic sort in LDS orders the <= k survivors on the 64-bit
-//      composite (key << 32 | ~index); the row is written with -1 / NaN
-//      padding.
+// Every candidate becomes the 64-bit composite (orderable score key << 32 |
+// ~index); the k largest composites are exactly the answer, whatever order
+// the candidates arrive in.  Selection runs in two passes over the row:
+//
+//   1. a 4096-bin histogram of the top 12 bits of the score key (LDS, wave-
+//      aggregated atomics) locates the bin b* that holds the k-th score;
+//   2. one pass appends every candidate above b* to the selected list and
+//      every candidate in b* to a candidate list (both in LDS); the
+//      candidate list is sorted (bitonic) and its best k - |above| entries
+//      complete the selection, which is sorted and written.
+//
+// A bin b* too large for the LDS candidate list (heavy exact ties) falls
+// back to an exact 8-bit radix select with an ordered tie scan, which needs
+// no buffer at all.  The passes keep four 16-byte loads per thread in
+// flight; when the rows are few (decode) a row gets a 1024-thread workgroup.
 //
 // Block-select output mode writes the kept blocks in ascending block order
 // with the forced first / local blocks added (score +inf).
+#include <algorithm>
+
 #include "tks_launch.hpp"
 
 namespace tks {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kMaxK = 2048;
+constexpr int kCap = 4096;          // LDS candidate list (entries of the threshold bin)
+constexpr int kBins = 4096;         // 12-bit first digit
+constexpr int kBinShift = 20;
 constexpr int kMaxBlkEntries = 512;
+
+// LDS of the selection kernels: selected list [0, kMaxK), candidate list
+// [kMaxK, kMaxK + kCap).  The histogram of pass 1 aliases the candidate
+// list; the radix fallback uses the selected list and 4 KiB after it.
+struct SelectLds {
+    uint64_t u[kMaxK + kCap];
+    int32_t blk[kMaxBlkEntries];
+    int32_t wsum[kMaxWaves];
+    int32_t pick[8];
+    int32_t cnt[2];
+};
+
+__device__ inline uint32_t* lds_hist(SelectLds& L) { return reinterpret_cast<uint32_t*>(&L.u[kMaxK]); }
 
 struct RowCtx {
     int64_t y;
     int32_t t;
-    int32_t lo, hi;        // valid score columns [lo, hi)
+    int32_t lo, hi;          // valid score columns [lo, hi)
     int32_t n_tok;
     bool prior;
     const float* srow;
-    const int32_t* blk_row;  // LDS copy in block mode
+    const int32_t* blk_row;  // block mode: LDS copy of the row's block list
 };
 
-// Visit candidate p of the row's index space (prior list first, then score
-// columns lo..hi-1).  Returns false for an empty / invalid slot.
-__device__ inline bool candidate(const SelectArgs& a, const RowCtx& r, int32_t p, uint32_t& key,
-                                 int32_t& idx) {
-    const int32_t np = r.prior ? a.topk : 0;
-    if (p < np) {
-        idx = a.prior_idx[r.y * a.topk + p];
-        if (idx < 0) return false;
-        key = score_key(a.prior_val[r.y * a.topk + p]);
-        return true;
-    }
-    const int32_t j = r.lo + (p - np);
-    if (j >= r.hi) return false;
-    if (a.blocks_mode) {
-        const int32_t b = r.blk_row[j >> a.block_shift];
-        if (b < 0 || r.n_tok <= 0 || b > ((r.n_tok - 1) >> a.block_shift)) return false;
-        idx = (b << a.block_shift) + (j & ((1 << a.block_shift) - 1));
-        if (idx >= r.n_tok) return false;
-    } else {
-        idx = a.col_key0 + j;
-    }
-    key = score_key(r.srow[j]);
-    return true;
+__device__ inline uint64_t composite(uint32_t key, int32_t idx) {
+    return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a, int64_t n_rows) {
-    __shared__ uint64_t s_sel[kMaxK];
-    __shared__ uint32_t s_hist[kWaves][256];
-    __shared__ int32_t s_blk[kMaxBlkEntries];
-    __shared__ int32_t s_wsum[kWaves];
-    __shared__ int32_t s_pick[4];
-    __shared__ int32_t s_cgt;
+// Key index of score column j, or -1 when the slot holds no candidate.
+__device__ inline int32_t column_index(const SelectArgs& a, const RowCtx& r, int32_t j) {
+    if (!a.blocks_mode) return a.col_key0 + j;
+    const int32_t b = r.blk_row[j >> a.block_shift];
+    if (b < 0 || r.n_tok <= 0 || b > ((r.n_tok - 1) >> a.block_shift)) return -1;
+    const int32_t idx = (b << a.block_shift) + (j & ((1 << a.block_shift) - 1));
+    return idx < r.n_tok ? idx : -1;
+}
 
+// Visit the candidates of columns [c_begin, c_end) of the row (subset of
+// [lo, hi)), thread-strided in groups of 4 consecutive columns, with U
+// groups loaded before any is processed.  Every thread calls f the same
+// number of times (valid = false past the end), so f may use wave-wide
+// ballots.
+template <bool VEC, int NT, class F>
+__device__ inline void visit_columns(const SelectArgs& a, const RowCtx& r, int32_t c_begin,
+                                     int32_t c_end, F&& f) {
+    constexpr int U = 4;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-
-    RowCtx r;
-    r.y = blockIdx.x;
-    if (r.y >= n_rows) return;
-    r.t = a.rows.query(r.y);
-    r.n_tok = a.vis.tokens(r.t);
-    const int32_t count = a.row_len ? a.row_len[r.y] : a.vis.count(r.t);
-
-    // Rows whose visible keys all lie before this tile finished earlier.
-    if (!a.always_final && a.tile_begin > 0 && count <= a.tile_begin) return;
-    const bool final_out = a.always_final || count <= a.tile_end;
-    r.prior = a.prior_val != nullptr && a.tile_begin > 0;
-
-    r.srow = a.scores + r.y * a.score_stride;
-    if (a.blocks_mode) {
-        r.lo = 0;
-        r.hi = a.n_cols;
-        const int32_t n_ent = a.n_cols >> a.block_shift;
-        const int32_t* src = a.blk + (a.rows.y0 + r.y) * a.blk_stride;
-        for (int i = tid; i < n_ent; i += kThreads) s_blk[i] = src[i];
-        r.blk_row = s_blk;
-    } else {
-        r.lo = a.col_lo;
-        r.hi = min(a.n_cols, max(0, count - a.col_key0));
-        r.blk_row = nullptr;
-    }
-    const int32_t n_slots = (r.prior ? a.topk : 0) + max(0, r.hi - r.lo);
-    const int32_t K = a.topk;
-
-    // ---- 1. radix select -------------------------------------------------
-    uint32_t prefix = 0;     // selected high bits
-    int shift_done = 32;     // bits >= shift_done are fixed in `prefix`
-    int32_t kr = K;          // rank still to place inside the current bucket
-    bool take_all = false;
-    int32_t total = 0;
-    for (int shift = 24; shift >= 0 && K > 0; shift -= 8) {
-        for (int i = tid; i < kWaves * 256; i += kThreads) (&s_hist[0][0])[i] = 0;
-        __syncthreads();
-        for (int32_t p = tid; p < n_slots; p += kThreads) {
-            uint32_t key;
-            int32_t idx;
-            if (!candidate(a, r, p, key, idx)) continue;
-            if (shift_done < 32 && (key >> shift_done) != (prefix >> shift_done)) continue;
-            atomicAdd(&s_hist[wave][(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // bins in descending order: position 4*lane + i is bin 255 - 4*lane - i
-            int32_t c[4];
-            int32_t lsum = 0;
+    if (c_begin >= c_end) return;
+    const int32_t base0 = c_begin & ~3;
+    // aligned groups past the end re-read the last group (inside the row's
+    // storage, whose stride is a multiple of 4): the vector loads need no
+    // branch, so all U of them stay in flight together
+    const int32_t last = (c_end - 1) & ~3;
+    for (int32_t base = base0; base < c_end; base += 4 * NT * U) {
+        float v[U][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int bin = 255 - (4 * lane + i);
-                int32_t v = 0;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) v += (int32_t)s_hist[w][bin];
-                c[i] = v;
-                lsum += v;
-            }
-            int32_t inc = lsum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int32_t v = __shfl_up(inc, o);
-                if (lane >= o) inc += v;
-            }
-            const int32_t excl = inc - lsum;
-            if (lane == 63) s_pick[3] = inc;  // candidates in the current bucket
-            if (excl < kr && kr <= inc) {
-                int32_t cum = excl;
+        for (int u = 0; u < U; ++u) {
+            const int32_t j0 = base + 4 * (u * NT + tid);
+            if (VEC) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(r.srow + min(j0, last));
+                v[u][0] = x[0]; v[u][1] = x[1]; v[u][2] = x[2]; v[u][3] = x[3];
+            } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (cum < kr && kr <= cum + c[i]) {
-                        s_pick[0] = 255 - (4 * lane + i);
-                        s_pick[1] = cum;
-                        s_pick[2] = c[i];
-                    }
-                    cum += c[i];
+                    const int32_t j = j0 + i;
+                    v[u][i] = (j >= c_begin && j < c_end) ? r.srow[j] : 0.0f;
                 }
             }
         }
-        __syncthreads();
-        const int32_t bucket_total = s_pick[3];
-        if (shift == 24) total = bucket_total;
-        if (bucket_total <= kr) {  // every candidate of the bucket is kept
-            take_all = shift == 24;
-            kr = bucket_total;
-            break;
-        }
-        const int32_t d = s_pick[0];
-        kr -= s_pick[1];
-        prefix |= (uint32_t)d << shift;
-        shift_done = shift;
-        const int32_t in_bucket = s_pick[2];
-        __syncthreads();
-        if (in_bucket == kr) break;  // the whole bucket is needed
-    }
-    if (K == 0) {
-        take_all = false;
-        kr = 0;
-        total = 0;
-    }
-
-    // ---- 2. ordered collection ------------------------------------------
-    // Selected = candidates whose bits above shift_done exceed the bucket
-    // prefix, plus the first `need` candidates inside the bucket.
-    int32_t need, n_gt;
-    if (take_all) {
-        need = 0;
-        n_gt = total;
-    } else {
-        need = kr;
-        n_gt = K - kr;
-    }
-    if (K == 0) n_gt = 0;
-    if (tid == 0) s_cgt = 0;
-    __syncthreads();
-    const uint32_t pb = shift_done < 32 ? (prefix >> shift_done) : 0u;
-    int32_t eq_base = 0;
-    for (int32_t base = 0; base < n_slots && K > 0; base += kThreads) {
-        const int32_t p = base + tid;
-        uint32_t key = 0;
-        int32_t idx = -1;
-        bool gt = false, eq = false;
-        if (p < n_slots && candidate(a, r, p, key, idx)) {
-            if (take_all || shift_done >= 32) {
-                gt = take_all;
-                eq = !take_all;
-            } else {
-                const uint32_t hi = key >> shift_done;
-                gt = hi > pb;
-                eq = hi == pb;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t j = base + 4 * (u * NT + tid) + i;
+                int32_t idx = -1;
+                if (j >= c_begin && j < c_end) idx = column_index(a, r, j);
+                f(idx >= 0, score_key(v[u][i]), idx);
             }
         }
-        const uint64_t comp = ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
-        if (gt) {
-            const int32_t pos = atomicAdd(&s_cgt, 1);
-            if (pos < K) s_sel[pos] = comp;
-        }
-        // workgroup-wide exclusive count of `eq` in slot order
-        const uint64_t bal = __ballot(eq);
-        const int32_t below = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) s_wsum[wave] = __popcll(bal);
-        __syncthreads();
-        int32_t off = 0, tot = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const int32_t c = s_wsum[w];
-            off += (w < wave) ? c : 0;
-            tot += c;
-        }
-        if (eq) {
-            const int32_t pos = eq_base + off + below;
-            if (pos < need) s_sel[n_gt + pos] = comp;
-        }
-        eq_base += tot;
-        __syncthreads();
     }
-    const int32_t n_sel = n_gt + need;
+}
 
-    // ---- 3. sort survivors ------------------------------------------------
-    if (a.blockselect) {
-        // ascending block index: composite with the index on top
-        for (int i = tid; i < n_sel; i += kThreads) {
-            const uint64_t c = s_sel[i];
-            const uint32_t key = (uint32_t)(c >> 32);
-            const uint32_t nidx = (uint32_t)c;  // 0xFFFFFFFF - idx
-            s_sel[i] = ((uint64_t)nidx << 32) | key;
+// Visit the prior list (running top-k of earlier key tiles).
+template <int NT, class F>
+__device__ inline void visit_prior(const SelectArgs& a, const RowCtx& r, F&& f) {
+    const int tid = threadIdx.x;
+    if (!r.prior) return;
+    for (int32_t base = 0; base < a.topk; base += NT) {
+        const int32_t p = base + tid;
+        int32_t idx = -1;
+        float v = 0.0f;
+        if (p < a.topk) {
+            idx = a.prior_idx[r.y * a.topk + p];
+            v = a.prior_val[r.y * a.topk + p];
+        }
+        f(idx >= 0, score_key(v), idx);
+    }
+}
+
+// Wave-aggregated LDS histogram increment.
+__device__ inline void hist_add(uint32_t* h, bool valid, uint32_t bin) {
+    const uint64_t act = __ballot(valid);
+    if (act == 0) return;
+    const int leader = __builtin_ctzll(act);
+    const uint32_t first = (uint32_t)__shfl((int)bin, leader);
+    const uint64_t same = __ballot(valid && bin == first);
+    if (same == act) {
+        if ((int)(threadIdx.x & 63) == leader) atomicAdd(&h[bin], (uint32_t)__popcll(act));
+    } else if (valid) {
+        atomicAdd(&h[bin], 1u);
+    }
+}
+
+// Wave-aggregated append: returns this lane's slot (or -1 if !pred).
+__device__ inline int32_t wave_append(int32_t* counter, bool pred) {
+    const uint64_t m = __ballot(pred);
+    if (m == 0) return -1;
+    const int lane = threadIdx.x & 63;
+    const int leader = __builtin_ctzll(m);
+    int32_t base = 0;
+    if (lane == leader) base = atomicAdd(counter, (int32_t)__popcll(m));
+    base = __shfl(base, leader);
+    return pred ? base + (int32_t)__popcll(m & ((1ull << lane) - 1ull)) : -1;
+}
+
+// Threshold of the k best from a histogram (bins in LDS or global memory,
+// read through `get`): pick = {b*, count above b*, count in b*, total}.
+template <int NT, class G>
+__device__ inline void find_threshold(G&& get, int32_t K, int32_t* pick, int32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kWaves = NT / kWave;
+    constexpr int per = kBins / NT;  // bins per thread, descending order
+    int32_t c[per];
+    int32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = (int32_t)get(kBins - 1 - (per * tid + i));
+        s += c[i];
+    }
+    int32_t inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int32_t off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        off += (w < wave) ? wsum[w] : 0;
+        total += wsum[w];
+    }
+    inc += off;
+    const int32_t excl = inc - s;
+    if (tid == 0) {
+        pick[3] = total;
+        pick[0] = -1;
+    }
+    __syncthreads();
+    if (total > K && excl < K && K <= inc) {
+        int32_t cum = excl;
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            if (cum < K && K <= cum + c[i]) {
+                pick[0] = kBins - 1 - (per * tid + i);
+                pick[1] = cum;
+                pick[2] = c[i];
+            }
+            cum += c[i];
         }
     }
+    __syncthreads();
+}
+
+// Sort u[0, n) descending (bitonic over the next power of two, zero padded,
+// at most cap entries).
+template <int NT>
+__device__ inline void sort_desc(uint64_t* u, int32_t n, int32_t cap) {
+    const int tid = threadIdx.x;
     int32_t P2 = 1;
-    while (P2 < n_sel) P2 <<= 1;
-    for (int i = n_sel + tid; i < P2; i += kThreads) s_sel[i] = 0;
+    while (P2 < n) P2 <<= 1;
+    if (P2 > cap) P2 = cap;
+    for (int i = n + tid; i < P2; i += NT) u[i] = 0;
     __syncthreads();
     for (int size = 2; size <= P2; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (P2 >> 1); i += kThreads) {
+            for (int i = tid; i < (P2 >> 1); i += NT) {
                 const int lo = 2 * i - (i & (stride - 1));
                 const int hi = lo + stride;
                 const bool desc = (lo & size) == 0;
-                const uint64_t x = s_sel[lo], z = s_sel[hi];
+                const uint64_t x = u[lo], z = u[hi];
                 if ((x < z) == desc) {
-                    s_sel[lo] = z;
-                    s_sel[hi] = x;
+                    u[lo] = z;
+                    u[hi] = x;
                 }
             }
             __syncthreads();
         }
     }
+}
 
-    // ---- 4. write ---------------------------------------------------------
+// Write a finished row: sel[0, n_sel) sorted descending on the composite.
+template <int NT>
+__device__ inline void write_row(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t n_sel,
+                                 bool final_out) {
+    const int tid = threadIdx.x;
+    uint64_t* sel = L.u;
     if (a.blockselect) {
-        const int32_t L = r.n_tok > 0 ? (r.n_tok - 1) / a.sel_block : -1;
-        const bool f_first = (a.force_flags & 1u) && L > 0;
-        const bool f_local = (a.force_flags & 2u) && L >= 0;
+        // ascending block index: re-key with the index on top and sort again
+        for (int i = tid; i < n_sel; i += NT) {
+            const uint64_t c = sel[i];
+            sel[i] = ((uint64_t)(uint32_t)c << 32) | (c >> 32);
+        }
+        __syncthreads();
+        sort_desc<NT>(sel, n_sel, kMaxK);
+        const int32_t Lb = r.n_tok > 0 ? (r.n_tok - 1) / a.sel_block : -1;
+        const bool f_first = (a.force_flags & 1u) && Lb > 0;
+        const bool f_local = (a.force_flags & 2u) && Lb >= 0;
         const int64_t g = a.rows.y0 + r.y;
         int32_t* oi = a.out_idx + g * a.out_width;
         float* ov = a.out_val ? a.out_val + g * a.out_width : nullptr;
         const int32_t off = f_first ? 1 : 0;
-        for (int j = tid; j < a.out_width; j += kThreads) {
+        for (int j = tid; j < a.out_width; j += NT) {
             int32_t id = -1;
             float v = __builtin_nanf("");
             if (f_first && j == 0) {
                 id = 0;
                 v = __builtin_inff();
             } else if (j - off < n_sel) {
-                const uint64_t c = s_sel[j - off];
+                const uint64_t c = sel[j - off];
                 id = (int32_t)(0xFFFFFFFFu - (uint32_t)(c >> 32));
                 v = key_score((uint32_t)c);
             } else if (f_local && j == off + n_sel) {
-                id = L;
+                id = Lb;
                 v = __builtin_inff();
             }
             oi[j] = id;
@@ -304,11 +292,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a, int64_t 
         oi = a.run_idx + r.y * a.topk;
         ov = a.run_val + r.y * a.topk;
     }
-    for (int j = tid; j < K; j += kThreads) {
+    for (int j = tid; j < a.topk; j += NT) {
         int32_t id = -1;
         float v = __builtin_nanf("");
         if (j < n_sel) {
-            const uint64_t c = s_sel[j];
+            const uint64_t c = sel[j];
             id = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
             v = key_score((uint32_t)(c >> 32));
         }
@@ -317,12 +305,262 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a, int64_t 
     }
 }
 
+// Exact fallback for a threshold bin larger than the LDS candidate list:
+// 8-bit radix select over the whole row (prior list first, then columns in
+// key-index order, so "first in scan order" is "lowest index" among equal
+// scores), then an ordered scan that collects the winners.  Fills
+// L.u[0, n) and returns n.
+template <bool VEC, int NT>
+__device__ int32_t radix_fallback(const SelectArgs& a, const RowCtx& r, SelectLds& L) {
+    constexpr int kWaves = NT / kWave;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t K = a.topk;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(&L.u[kMaxK]);  // [kWaves][256]
+    uint32_t prefix = 0;
+    int shift_done = 32;
+    int32_t kr = K;
+    bool take_all = false;
+    int32_t total = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < kWaves * 256; i += NT) hist[i] = 0;
+        __syncthreads();
+        auto f = [&](bool valid, uint32_t key, int32_t) {
+            valid = valid && (shift_done >= 32 || (key >> shift_done) == (prefix >> shift_done));
+            if (valid) atomicAdd(&hist[wave * 256 + ((key >> shift) & 255u)], 1u);
+        };
+        visit_prior<NT>(a, r, f);
+        visit_columns<VEC, NT>(a, r, r.lo, r.hi, f);
+        __syncthreads();
+        if (wave == 0) {
+            int32_t c[4], lsum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int bin = 255 - (4 * lane + i);
+                int32_t v = 0;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) v += (int32_t)hist[w * 256 + bin];
+                c[i] = v;
+                lsum += v;
+            }
+            int32_t inc = lsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int32_t v = __shfl_up(inc, o);
+                if (lane >= o) inc += v;
+            }
+            const int32_t excl = inc - lsum;
+            if (lane == 63) L.pick[3] = inc;
+            if (excl < kr && kr <= inc) {
+                int32_t cum = excl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (cum < kr && kr <= cum + c[i]) {
+                        L.pick[0] = 255 - (4 * lane + i);
+                        L.pick[1] = cum;
+                        L.pick[2] = c[i];
+                    }
+                    cum += c[i];
+                }
+            }
+        }
+        __syncthreads();
+        const int32_t bucket_total = L.pick[3];
+        if (shift == 24) total = bucket_total;
+        if (bucket_total <= kr) {
+            take_all = shift == 24;
+            kr = bucket_total;
+            break;
+        }
+        kr -= L.pick[1];
+        prefix |= (uint32_t)L.pick[0] << shift;
+        shift_done = shift;
+        const int32_t in_bucket = L.pick[2];
+        __syncthreads();
+        if (in_bucket == kr) break;
+    }
+    const int32_t need = take_all ? 0 : kr;
+    const int32_t n_gt = take_all ? total : K - kr;
+    if (tid == 0) L.cnt[0] = 0;
+    __syncthreads();
+    const uint32_t pb = shift_done < 32 ? (prefix >> shift_done) : 0u;
+    int32_t eq_base = 0;
+    auto g = [&](bool valid, uint32_t key, int32_t idx) {
+        bool gt = false, eq = false;
+        if (valid) {
+            if (take_all || shift_done >= 32) {
+                gt = take_all;
+            } else {
+                const uint32_t hi = key >> shift_done;
+                gt = hi > pb;
+                eq = hi == pb;
+            }
+        }
+        const int32_t pos = wave_append(&L.cnt[0], gt);
+        if (gt && pos < K) L.u[pos] = composite(key, idx);
+        // workgroup-wide ordered count of `eq`
+        const uint64_t bal = __ballot(eq);
+        const int32_t below = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) L.wsum[wave] = __popcll(bal);
+        __syncthreads();
+        int32_t off = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            off += (w < wave) ? L.wsum[w] : 0;
+            tot += L.wsum[w];
+        }
+        if (eq) {
+            const int32_t p = eq_base + off + below;
+            if (p < need) L.u[n_gt + p] = composite(key, idx);
+        }
+        eq_base += tot;
+        __syncthreads();
+    };
+    // ordered scan: one candidate per thread per round (scalar) keeps order
+    if (r.prior) visit_prior<NT>(a, r, g);
+    {
+        RowCtx rr = r;
+        for (int32_t base = r.lo; base < r.hi; base += NT) {
+            const int32_t j = base + tid;
+            int32_t idx = -1;
+            float v = 0.0f;
+            if (j < r.hi) {
+                idx = column_index(a, rr, j);
+                v = r.srow[j];
+            }
+            g(idx >= 0, score_key(v), idx);
+        }
+    }
+    __syncthreads();
+    return n_gt + need;
+}
+
+// Finish after pass 2: sel[0, n_gt) filled; cand[0, n_cand) holds the
+// threshold bin; take its best `need`.  Returns the selected count.
+template <int NT>
+__device__ inline int32_t finish_from_candidates(SelectLds& L, int32_t n_gt, int32_t n_cand,
+                                                 int32_t need) {
+    const int tid = threadIdx.x;
+    uint64_t* cand = &L.u[kMaxK];
+    if (need > 0) {
+        sort_desc<NT>(cand, n_cand, kCap);
+        for (int i = tid; i < need; i += NT) L.u[n_gt + i] = cand[i];
+    }
+    __syncthreads();
+    return n_gt + need;
+}
+
+template <int NT>
+__device__ inline void setup_row(const SelectArgs& a, RowCtx& r, SelectLds& L, int64_t y,
+                                 int32_t& count) {
+    const int tid = threadIdx.x;
+    r.y = y;
+    r.t = a.rows.query(y);
+    r.n_tok = a.vis.tokens(r.t);
+    count = a.row_len ? a.row_len[y] : a.vis.count(r.t);
+    r.prior = a.prior_val != nullptr && a.tile_begin > 0;
+    r.srow = a.scores + y * a.score_stride;
+    if (a.blocks_mode) {
+        r.lo = 0;
+        r.hi = a.n_cols;
+        const int32_t n_ent = a.n_cols >> a.block_shift;
+        const int32_t* src = a.blk + (a.rows.y0 + y) * a.blk_stride;
+        for (int i = tid; i < n_ent; i += NT) L.blk[i] = src[i];
+        r.blk_row = L.blk;
+    } else {
+        r.lo = a.col_lo;
+        r.hi = min(a.n_cols, max(0, count - a.col_key0));
+        r.blk_row = nullptr;
+    }
+}
+
+// ------------------------------------------------- one workgroup per row
+
+template <bool VEC, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows) {
+    __shared__ SelectLds L;
+    const int tid = threadIdx.x;
+    if ((int64_t)blockIdx.x >= n_rows) return;
+    RowCtx r;
+    int32_t count;
+    setup_row<NT>(a, r, L, blockIdx.x, count);
+    if (!a.always_final && a.tile_begin > 0 && count <= a.tile_begin) return;
+    const bool final_out = a.always_final || count <= a.tile_end;
+    const int32_t K = a.topk;
+    uint32_t* hist = lds_hist(L);
+
+    int32_t n_sel = 0;
+    if (K > 0) {
+        // pass 1: 12-bit histogram
+        for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+        __syncthreads();
+        auto h = [&](bool valid, uint32_t key, int32_t) { hist_add(hist, valid, key >> kBinShift); };
+        visit_prior<NT>(a, r, h);
+        visit_columns<VEC, NT>(a, r, r.lo, r.hi, h);
+        __syncthreads();
+        find_threshold<NT>([&](int b) { return hist[b]; }, K, L.pick, L.wsum);
+        const int32_t bstar = L.pick[0];
+        const int32_t above = L.pick[1], inbin = L.pick[2], total = L.pick[3];
+        __syncthreads();
+        if (bstar >= 0 && inbin > kCap && inbin != K - above) {
+            n_sel = radix_fallback<VEC, NT>(a, r, L);
+        } else {
+            // pass 2: collect
+            const bool all = bstar < 0;                    // total <= K
+            const bool whole_bin = !all && inbin == K - above;
+            if (tid == 0) {
+                L.cnt[0] = 0;
+                L.cnt[1] = 0;
+            }
+            __syncthreads();
+            auto c = [&](bool valid, uint32_t key, int32_t idx) {
+                const uint32_t bin = key >> kBinShift;
+                const bool to_sel = valid && (all || (int32_t)bin > bstar ||
+                                              (whole_bin && (int32_t)bin == bstar));
+                const bool to_cand = valid && !all && !whole_bin && (int32_t)bin == bstar;
+                const int32_t ps = wave_append(&L.cnt[0], to_sel);
+                if (to_sel && ps < kMaxK) L.u[ps] = composite(key, idx);
+                const int32_t pc = wave_append(&L.cnt[1], to_cand);
+                if (to_cand && pc < kCap) L.u[kMaxK + pc] = composite(key, idx);
+            };
+            visit_prior<NT>(a, r, c);
+            visit_columns<VEC, NT>(a, r, r.lo, r.hi, c);
+            __syncthreads();
+            if (all)
+                n_sel = total;
+            else if (whole_bin)
+                n_sel = K;
+            else
+                n_sel = finish_from_candidates<NT>(L, above, inbin, K - above);
+        }
+    }
+    __syncthreads();
+    sort_desc<NT>(L.u, n_sel, kMaxK);
+    write_row<NT>(a, r, L, n_sel, final_out);
+}
+
+bool vec_ok(const SelectArgs& a) {
+    return (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0) && (a.score_stride % 4 == 0);
+}
+
+template <int NT>
+void launch_nt(const SelectArgs& a, int64_t n_rows, hipStream_t stream) {
+    if (vec_ok(a))
+        hipLaunchKernelGGL((select_kernel<true, NT>), dim3((unsigned)n_rows), dim3(NT), 0, stream,
+                           a, n_rows);
+    else
+        hipLaunchKernelGGL((select_kernel<false, NT>), dim3((unsigned)n_rows), dim3(NT), 0, stream,
+                           a, n_rows);
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(kThreads), 0, stream, a,
-                       n_rows);
+    // few rows: a wide workgroup per row; many rows: several narrow ones per CU
+    if (n_rows < 512)
+        launch_nt<1024>(a, n_rows, stream);
+    else
+        launch_nt<256>(a, n_rows, stream);
     return hipGetLastError();
 }
 
