@@ -231,55 +231,60 @@ def main():
             speedup_vs_flat_with_pool=round(flat_ms / (hisa_ms + pool_ms), 3),
             iou_vs_flat_mean=round(float(np.mean(ious)), 4))
     else:
-        hisa_pairs = 0
+        hisa_pairs = block_pairs = tok = 0
     out["flat"] = dict(ms_per_layer=round(flat_ms, 4), qk_scores=flat_pairs,
                        qk_scores_per_s=flat_pairs / (flat_ms * 1e-3))
     total_pairs = flat_pairs + hisa_pairs
     value = total_pairs / (ms_step * 1e-3)
 
-    # ---- roofline of the dominant kernel
-    kb = cfg.dim * (1 if cfg.key_dtype else 2) + (4 if cfg.key_dtype else 0)
+    # ---- roofline of the dominant kernel: algorithmic bytes and flops of
+    # one launch (per-unit figures times the units one launch processes)
+    kb = cfg.dim * (1 if cfg.key_dtype else 2) + (4 if cfg.key_dtype else 0)  # key + scale
     flops_pair = 2 * cfg.heads * cfg.dim
-    qw = cfg.heads * (cfg.dim * 2 + 4)
-    algo = {}
-    if "score_flat" in roles:
-        n_launch = roles["score_flat"][1] / args.steps
-        shared = cfg.n_q > 1        # prefill: keys shared by the query rows
-        bytes_ = flat_pairs * 4 + R * qw + (cfg.batch * cfg.n_k * kb if shared else flat_pairs * kb)
-        algo["score_flat"] = (bytes_ / n_launch, flat_pairs * flops_pair / n_launch)
-    if "pool" in roles:
-        nb = cfg.n_k // cfg.block
-        bytes_ = cfg.batch * nb * cfg.block * kb + cfg.batch * nb * cfg.dim * 2
-        algo["pool"] = (bytes_, 0.0)
-    if "score_refine" in roles and hisa:
-        n_launch = roles["score_refine"][1] / args.steps
-        algo["score_refine"] = ((tok * (kb + 4) + R * qw) / n_launch, tok * flops_pair / n_launch)
-    if "score_pooled" in roles and hisa:
-        n_launch = roles["score_pooled"][1] / args.steps
-        algo["score_pooled"] = ((block_pairs * 4 + R * qw + cfg.batch * (cfg.n_k // cfg.block) *
-                                 cfg.dim * 2) / n_launch, block_pairs * flops_pair / n_launch)
+    qw = cfg.heads * (cfg.dim * 2 + 4)                                          # q row + w row
+    nb = cfg.n_k // cfg.block if hisa else 0
+    units = {}  # role -> (bytes, flops) per step
+    shared = cfg.n_q > 1  # prefill: key rows are shared by the query rows
+    units["score_flat"] = (flat_pairs * 4 + R * qw +
+                           (cfg.batch * cfg.n_k * kb if shared else flat_pairs * kb),
+                           flat_pairs * flops_pair)
+    units["select_flat"] = (flat_pairs * 4 + R * K * 8, 0)
+    if hisa:
+        units["pool"] = (cfg.batch * nb * cfg.block * kb + cfg.batch * nb * cfg.dim * 2, 0)
+        units["score_pooled"] = (block_pairs * 4 + R * qw + cfg.batch * nb * cfg.dim * 2,
+                                 block_pairs * flops_pair)
+        units["select_pooled"] = (block_pairs * 4 + R * cfg.m_total * 4, 0)
+        units["score_refine"] = (tok * (kb + 4) + R * qw + R * cfg.m_total * 4,
+                                 tok * flops_pair)
+        units["select_refine"] = (tok * 4 + R * cfg.m_total * 4 + R * K * 8, 0)
     dom = max(roles, key=lambda r: roles[r][0])
     tot, n = roles[dom]
     avg_ms = tot / n
-    roof = None
-    if dom in algo:
-        b, f = algo[dom]
-        ai = f / b if b else 0.0
-        if ai > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-            ach = f / (avg_ms * 1e-3) / 1e12
-            roof = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
-        else:
-            ach = b / (avg_ms * 1e-3) / 1e9
-            roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(ach / HBM_PEAK_GBS, 4))
-        roof.update(kernel=dom, avg_launch_ms=round(avg_ms, 5),
-                    algorithmic_bytes_per_launch=int(b), algorithmic_flops_per_launch=int(f))
-        src = {"score_flat": ["score.hip"], "score_refine": ["score.hip"],
-               "score_pooled": ["score.hip"], "pool": ["pool.hip"], "select": ["select.hip"]}[dom]
-        roof["traffic"] = pmc_traffic(dom, cfg.name, src)
-    kern = {r: dict(avg_ms=round(t / n, 5), launches_per_step=n / args.steps)
-            for r, (t, n) in roles.items()}
+    per_launch = n / args.steps
+    b, f = units[dom]
+    b, f = b / per_launch, f / per_launch
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if f and f / b > ridge:
+        ach = f / (avg_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
+    else:
+        ach = b / (avg_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4))
+    src = {"pool": ["pool.hip"]}.get(dom, ["score.hip"] if dom.startswith("score") else
+                                       ["select.hip"])
+    roof["traffic"] = pmc_traffic(dom, cfg.name, src)
+    roof.update(kernel=dom, avg_launch_ms=round(avg_ms, 5),
+                algorithmic_bytes_per_launch=int(b), algorithmic_flops_per_launch=int(f))
+    kern = {}
+    for r, (t, nl) in roles.items():
+        rb, rf = units.get(r, (0, 0))
+        pl = nl / args.steps
+        ms = t / nl
+        kern[r] = dict(avg_ms=round(ms, 5), launches_per_step=pl,
+                       gb_per_s=round(rb / pl / (ms * 1e-3) / 1e9, 1) if rb else None,
+                       tflop_per_s=round(rf / pl / (ms * 1e-3) / 1e12, 2) if rf else None)
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None

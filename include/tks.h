@@ -121,8 +121,8 @@ int tks_topk_flat(const tks_shape* shape, const void* q, const float* w, const v
  * scores + r * row_stride (row_len NULL: n_cols for every row); candidate j
  * of a row is key index j.  Scores must not be NaN.
  *   idx / vals: [n_rows, topk] (vals may be NULL).
- *   workspace: tks_topk_scores_workspace(n_rows, n_cols, topk) bytes (currently
- *   0 for every size; NULL is then accepted).
+ *   workspace: tks_topk_scores_workspace(n_rows, n_cols, topk) bytes, 256-byte
+ *   aligned (0 -- and NULL accepted -- unless the rows are few and long).
  */
 size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk);
 int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,
@@ -183,11 +183,14 @@ int tks_hisa_refine_topk(const tks_shape* shape, const void* q, const float* w, 
  * HIP events recorded on the launch's stream.  tks_profile_enable(1) clears
  * earlier records.  tks_profile_read() waits for the recorded events and
  * returns the summed duration and launch count of one kernel role:
- *   "score_flat"   -- token scoring of tks_topk_flat / tks_indexer_scores
- *   "score_pooled" -- pooled-block scoring of tks_hisa_block_select
- *   "score_refine" -- gathered-block scoring of tks_hisa_refine_topk
- *   "select"       -- every top-k selection launch
- *   "pool"         -- tks_hisa_pool_keys
+ *   "score_flat"    -- token scoring of tks_topk_flat / tks_indexer_scores
+ *   "score_pooled"  -- pooled-block scoring of tks_hisa_block_select
+ *   "score_refine"  -- gathered-block scoring of tks_hisa_refine_topk
+ *   "select_flat"   -- top-k selection of tks_topk_flat
+ *   "select_pooled" -- block selection of tks_hisa_block_select
+ *   "select_refine" -- top-k selection of tks_hisa_refine_topk
+ *   "select_scores" -- tks_topk_scores
+ *   "pool"          -- tks_hisa_pool_keys
  * Returns TKS_EINVAL for an unknown role or NULL outputs.
  */
 int tks_profile_enable(int on);

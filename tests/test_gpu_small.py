@@ -210,6 +210,32 @@ def test_fp8_keys_integer_exact():
     assert_topk_exact(gi, gv, oi, ov, "fp8")
 
 
+@pytest.mark.parametrize("dim,heads", [(128, 64), (64, 8), (32, 33)])
+def test_fp8_decode_stream_path_exact(dim, heads):
+    """One query per sequence (decode): keys are streamed through the LDS
+    ring kernel.  Integer codes with power-of-two scales keep every score
+    exact, so flat and HISA must equal the oracle bit for bit."""
+    say("fp8 decode stream path dim %d heads %d" % (dim, heads))
+    n_k = 5000
+    sh, x = int_case(40 + dim, batch=5, n_q=1, n_k=n_k, heads=heads, dim=dim, q_pos0=n_k - 1,
+                     fp8=True)
+    oi, ov = oracle_flat(sh, x, 300)
+    gi, gv = gpu_flat(sh, x, 300)
+    assert_topk_exact(gi, gv, oi, ov, "fp8 decode flat")
+    R = 5
+    rows = np.arange(R)
+    qr, wr = x["q"].reshape(R, heads, dim), x["w"].reshape(R, heads)
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], x["k_scale"], 128, 6,
+                                      FORCE_FIRST | FORCE_LOCAL, 300, rows)
+    q, w, k, ks = gpu_inputs(x)
+    idx, vals, blk = tks.hisa_topk(tks.Shape(**sh), q, w, k, ks, 128, 6, FORCE_FIRST | FORCE_LOCAL,
+                                   300)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                      "fp8 decode hisa")
+
+
 def test_fp8_every_code_decodes_exactly():
     """One-hot keys: key c holds e4m3fn code c at dim 0, so its score is
     max(0, q0 * value(c)); compared with torch's e4m3fn decode."""
@@ -254,7 +280,8 @@ def brute(scores, n, k):
     return out
 
 
-@pytest.mark.parametrize("n_cols,topk", [(5000, 2048), (70000, 2048), (300, 64), (1, 1)])
+@pytest.mark.parametrize("n_cols,topk", [(5000, 2048), (70000, 2048), (140000, 2048), (300, 64),
+                                         (1, 1)])
 def test_topk_scores_matches_full_sort(n_cols, topk):
     say("topk_scores n_cols=%d k=%d" % (n_cols, topk))
     rng = np.random.default_rng(n_cols)
@@ -264,8 +291,14 @@ def test_topk_scores_matches_full_sort(n_cols, topk):
     sc[2] = -0.0
     sc[3] = rng.standard_normal(n_cols).astype(np.float32)
     sc[4, ::2] = -np.inf
+    # the k best all in one column partition: the two-stage selection for few
+    # long rows must detect the truncated partition and recompute exactly
+    sc[5] = np.arange(n_cols, dtype=np.float32)
+    sc[6] = -np.arange(n_cols, dtype=np.float32)
+    sc[7] = np.where(np.arange(n_cols) % 3 == 0, 5.0, rng.standard_normal(n_cols)).astype(np.float32)
     row_len = rng.integers(0, n_cols + 1, R).astype(np.int32)
     row_len[0] = n_cols
+    row_len[5:8] = n_cols
     idx, vals = tks.topk_scores(dev(sc), topk, dev(row_len))
     torch.cuda.synchronize()
     gi, gv = host(idx), host(vals)

@@ -140,7 +140,8 @@ struct FlatPlan {
     int32_t q_chunk;
     int32_t k_tile;
     int64_t score_stride;
-    size_t off_scores, off_run_val, off_run_idx, bytes;
+    tks::SelectSplit split;  // two-stage selection of few long rows (one tile)
+    size_t off_scores, off_run_val, off_run_idx, off_split, bytes;
 };
 
 FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile) {
@@ -170,6 +171,10 @@ FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_
     if (tiled) off += round_up(qc * (int64_t)topk * 4, 256);
     p.off_run_idx = off;
     if (tiled) off += round_up(qc * (int64_t)topk * 4, 256);
+    p.split = tiled ? tks::SelectSplit{0, 0, 0}
+                    : tks::select_split(qc, (int32_t)std::min<int64_t>(kt, maxvis), topk);
+    p.off_split = off;
+    off += tks::select_split_workspace(qc, p.split);
     p.bytes = off;
     return p;
 }
@@ -274,6 +279,7 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
             a.n_cols = std::max(0, te - tb);
             a.out = sbuf;
             a.out_stride = p.score_stride;
+            a.stream_keys = s->n_q == 1;
             hipError_t e;
             {
                 Timed tm("score_flat", stream);
@@ -300,8 +306,11 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
             sa.tile_begin = tb;
             sa.tile_end = ti + 1 == n_tiles ? INT32_MAX : te;
             {
-                Timed tm("select", stream);
-                e = tks::launch_select(sa, n, stream);
+                Timed tm("select_flat", stream);
+                if (p.split.parts > 0 && n_tiles == 1)
+                    e = tks::launch_select_split(sa, n, p.split, ws + p.off_split, stream);
+                else
+                    e = tks::launch_select(sa, n, stream);
             }
             if (e != hipSuccess) return hip_fail(e, "select launch");
         }
@@ -310,10 +319,8 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
 }
 
 size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk) {
-    (void)n_rows;
-    (void)n_cols;
-    (void)topk;
-    return 0;
+    if (n_rows < 0 || n_cols < 0 || topk < 1 || topk > kMaxTopk) return 0;
+    return tks::select_split_workspace(n_rows, tks::select_split(n_rows, n_cols, topk));
 }
 
 int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,
@@ -340,12 +347,17 @@ int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t
     sa.out_idx = idx;
     sa.out_width = topk;
     sa.always_final = 1;
-    (void)workspace;
-    (void)workspace_bytes;
+    const tks::SelectSplit sp = tks::select_split(n_rows, n_cols, topk);
+    const size_t need = tks::select_split_workspace(n_rows, sp);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(TKS_EWORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                    need);
+    if (need && !aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
     hipError_t e;
     {
-        Timed tm("select", stream);
-        e = tks::launch_select(sa, n_rows, stream);
+        Timed tm("select_scores", stream);
+        e = sp.parts > 0 ? tks::launch_select_split(sa, n_rows, sp, workspace, stream)
+                         : tks::launch_select(sa, n_rows, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "select launch");
     return TKS_OK;
@@ -474,7 +486,7 @@ int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, con
         sa.force_flags = force_flags;
         sa.sel_block = block;
         {
-            Timed tm("select", stream);
+            Timed tm("select_pooled", stream);
             e = tks::launch_select(sa, n, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "block select launch");
@@ -558,6 +570,7 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
         a.block_shift = bs;
         a.out = sbuf;
         a.out_stride = p.stride;
+        a.stream_keys = s->n_q == 1;
         hipError_t e;
         {
             Timed tm("score_refine", stream);
@@ -581,7 +594,7 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
         sa.out_width = topk;
         sa.always_final = 1;
         {
-            Timed tm("select", stream);
+            Timed tm("select_refine", stream);
             e = tks::launch_select(sa, n, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "refine select launch");
@@ -597,7 +610,8 @@ int tks_profile_enable(int on) {
 }
 
 int tks_profile_read(const char* role, double* total_ms, int64_t* launches) {
-    static const char* kRoles[] = {"score_flat", "score_pooled", "score_refine", "select", "pool"};
+    static const char* kRoles[] = {"score_flat",   "score_pooled",  "score_refine", "select_flat",
+                                   "select_pooled", "select_refine", "select_scores", "pool"};
     if (!role || !total_ms || !launches) return fail(TKS_EINVAL, "NULL argument");
     bool known = false;
     for (const char* r : kRoles) known = known || strcmp(r, role) == 0;

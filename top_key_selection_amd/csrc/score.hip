@@ -48,6 +48,13 @@ __device__ inline void load_key(KeyFrag<D, FP8>& f, const void* k, int64_t row, 
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// max(0, x) in one integer max on the bit pattern: negative floats (and -0)
+// are negative integers, non-negative floats keep their order.  Inputs are
+// finite, so no NaN handling is needed.
+__device__ __forceinline__ float relu_bits(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // B operand of k-step ks from a key fragment.
 template <int D, bool FP8>
 __device__ inline bf16x8 key_operand(const KeyFrag<D, FP8>& f, int ks) {
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], fmaxf(acc[mb][i], 0.0f), sc);
+            for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
         sc += __shfl_xor(sc, 32);
         if (FP8) sc *= scale;
         const int32_t slot = j + m;
@@ -225,9 +232,226 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
     }
 }
 
+// ------------------------------------------------------------------------
+// fp8 keys streamed once (decode, gathered refinement): every wave keeps a
+// ring of R sub-blocks in flight through LDS.  Each lane copies its own key
+// fragment (and the key's scale) with direct global->LDS loads that hold no
+// VGPRs while in flight and bypass the caches' reuse policy (nontemporal);
+// the lane reads the fragment back itself, so the ring needs no barrier.
+// The compiler cannot see which LDS slot a copy lands in, so the ring is
+// read with inline-asm LDS loads and the wait for stage t is an explicit
+// vmcnt: after stage t's copies the wave issues the copies of the R - 1
+// later stages (CH + 1 each) and possibly stores, which only raise the
+// count, so vmcnt((R - 1) * (CH + 1)) guarantees stage t has landed.
+
+template <int D>
+struct Fp8Ring {
+    static constexpr int R = 4;                       // stages in flight per wave
+    static constexpr int CH = D / 32;                 // 16-byte chunks per lane and key
+    static constexpr int STAGE = CH * 1024 + 256;     // chunk slabs + per-lane scales
+    static constexpr int WAVE = R * STAGE;
+};
+
+// Read one ring stage (CH 16-byte chunks 1 KiB apart, and the scale) with a
+// single wait; early-clobber outputs keep every address register intact
+// while the reads are in flight.
+template <int CH>
+__device__ __forceinline__ void lds_read_stage(uint32_t addr, uint32_t saddr, u32x4* raw,
+                                               float& scale) {
+    if constexpr (CH == 4) {
+        asm volatile(
+            "ds_read_b128 %0, %5\n\t"
+            "ds_read_b128 %1, %5 offset:1024\n\t"
+            "ds_read_b128 %2, %5 offset:2048\n\t"
+            "ds_read_b128 %3, %5 offset:3072\n\t"
+            "ds_read_b32 %4, %6\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(scale)
+            : "v"(addr), "v"(saddr));
+    } else if constexpr (CH == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %3 offset:1024\n\t"
+            "ds_read_b32 %2, %4\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(scale)
+            : "v"(addr), "v"(saddr));
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b32 %1, %3\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(raw[0]), "=&v"(scale)
+            : "v"(addr), "v"(saddr));
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+template <int D, int MB, bool BLOCKS>
+__global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_rows,
+                                                        int32_t seg_slots) {
+    using RG = Fp8Ring<D>;
+    constexpr int KS = D / 16;
+    __shared__ __align__(16) uint8_t ring[4 * RG::WAVE];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int hf = lane >> 5;
+
+    const int64_t y = blockIdx.x;
+    if (y >= n_rows) return;
+    const int32_t seq = a.rows.seq(y);
+    const int32_t t = a.rows.query(y);
+    const int64_t qr = a.rows.qrow(y);
+    const int32_t n_tok = a.vis.tokens(t);
+    const int32_t slot_begin = blockIdx.y * seg_slots;
+    const int32_t slot_end = min(a.n_cols, slot_begin + seg_slots);
+    const int32_t limit = BLOCKS ? slot_end : min(slot_end, max(0, a.vis.count(t) - a.col_key0));
+    const int32_t work_end = a.write_masked ? slot_end : limit;
+    if (slot_begin >= work_end) return;
+
+    bf16x8 qa[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int h = mb * 32 + m;
+        const int hc = h < a.heads ? h : 0;
+        const u32x4* p = reinterpret_cast<const u32x4*>(a.q + (qr * a.heads + hc) * D + hf * (D / 2));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = p[ks];
+            qa[mb][ks] = __builtin_bit_cast(bf16x8, h < a.heads ? v : u32x4{0, 0, 0, 0});
+        }
+    }
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int h = mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
+            wv[mb][j] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+        }
+
+    const int64_t kseq = (int64_t)seq * a.k_seq_len;
+    const int32_t* blk_row = BLOCKS ? a.blk + (a.rows.y0 + y) * a.blk_stride : nullptr;
+    const int32_t bmask = (1 << a.block_shift) - 1;
+    auto key_of = [&](int32_t slot, bool& valid) -> int32_t {
+        if (BLOCKS) {
+            const int32_t b = slot < limit ? blk_row[slot >> a.block_shift] : -1;
+            const bool ok = b >= 0 && b <= ((n_tok - 1) >> a.block_shift);
+            const int32_t key = ok ? (b << a.block_shift) + (slot & bmask) : 0;
+            valid = ok && key < n_tok;
+            return key;
+        }
+        valid = slot < limit;
+        return a.col_key0 + slot;
+    };
+
+    uint8_t* wring = ring + wave * RG::WAVE;
+    const uint32_t wring_addr = (uint32_t)(uintptr_t)wring;
+    // sub-block u of this wave covers slots first + u * 128 .. + 31
+    const int32_t first = slot_begin + wave * 32;
+    const int32_t nsub = first < work_end ? (work_end - first + 127) / 128 : 0;
+
+    auto fetch = [&](int32_t u) {
+        bool valid;
+        const int32_t key = key_of(first + u * 128 + m, valid);
+        const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k) + row * D + hf * (D / 2);
+        uint8_t* st = wring + (u % RG::R) * RG::STAGE;
+#pragma unroll
+        for (int c = 0; c < RG::CH; ++c)
+            __builtin_amdgcn_global_load_lds(src + c * 16, st + c * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.k_scale + row, st + RG::CH * 1024, 4, 0, 0);
+    };
+
+    // MFMAs of sub-block u, from the ring slot it occupies
+    auto mfma_stage = [&](int32_t u, f32x16* acc, float& scale) {
+        wait_vmcnt<(RG::R - 1) * (RG::CH + 1)>();
+        const uint32_t st = wring_addr + (u % RG::R) * RG::STAGE;
+        u32x4 raw[RG::CH];
+        lds_read_stage<RG::CH>(st + lane * 16, st + RG::CH * 1024 + lane * 4, raw, scale);
+        fetch(u + RG::R);  // refill the slot just read
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4& v = raw[ks >> 1];
+            const uint32_t d0 = (ks & 1) ? v[2] : v[0];
+            const uint32_t d1 = (ks & 1) ? v[3] : v[1];
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, false);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, true);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, false);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, true);
+            bf16x8 kb;
+            kb[0] = p0[0]; kb[1] = p0[1]; kb[2] = p1[0]; kb[3] = p1[1];
+            kb[4] = p2[0]; kb[5] = p2[1]; kb[6] = p3[0]; kb[7] = p3[1];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+        }
+    };
+    // ReLU * w head reduction and store of sub-block u
+    auto epilogue = [&](int32_t u, const f32x16* acc, float scale) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
+        sc += __shfl_xor(sc, 32);
+        sc *= scale;
+        const int32_t j = first + u * 128;
+        bool valid;
+        key_of(j + m, valid);
+        const int32_t slot = j + m;
+        if (hf == 0 && slot < slot_end) {
+            if (valid)
+                a.out[y * a.out_stride + slot] = sc;
+            else if (a.write_masked)
+                a.out[y * a.out_stride + slot] = -__builtin_inff();
+        }
+    };
+
+#pragma unroll
+    for (int u = 0; u < RG::R; ++u) fetch(u);
+    // two accumulator sets: the MFMAs of sub-block u + 1 are issued before the
+    // VALU epilogue of sub-block u, so the matrix and vector pipes overlap
+    f32x16 acc0[MB], acc1[MB];
+    float sc0 = 1.0f, sc1 = 1.0f;
+    if (nsub > 0) mfma_stage(0, acc0, sc0);
+    for (int32_t u = 0; u < nsub; u += 2) {
+        if (u + 1 < nsub) mfma_stage(u + 1, acc1, sc1);
+        epilogue(u, acc0, sc0);
+        if (u + 1 >= nsub) break;
+        if (u + 2 < nsub) mfma_stage(u + 2, acc0, sc0);
+        epilogue(u + 1, acc1, sc1);
+    }
+    // drain the copies still in flight before the wave's LDS is released
+    wait_vmcnt<0>();
+}
+
 template <int D, int MB, bool FP8, bool BLOCKS>
 hipError_t launch_t(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
+    if (FP8 && a.stream_keys) {
+        // keys read once: fp8 LDS-ring streaming kernel, >= ~2048 workgroups
+        // about two long-lived workgroups per CU: each loads its row's q / w
+        // once and streams a long run of keys
+        const int64_t want = (n_rows * (int64_t)a.n_cols + 511) / 512;
+        int64_t seg = std::min<int64_t>(16384, std::max<int64_t>(128, (want + 127) / 128 * 128));
+        while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
+        dim3 grid((unsigned)n_rows, (unsigned)((a.n_cols + seg - 1) / seg));
+        hipLaunchKernelGGL((score_fp8_kernel<D, MB, BLOCKS>), grid, dim3(256), 0, stream, a, n_rows,
+                           (int32_t)seg);
+        return hipGetLastError();
+    }
     if (a.n_cols <= 1024 && !BLOCKS && n_rows >= 8192) {
         // many short rows: one wave per row
         dim3 grid((unsigned)((n_rows + 3) / 4));

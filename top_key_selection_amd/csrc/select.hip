@@ -52,7 +52,7 @@ struct SelectLds {
     int32_t cnt[2];
 };
 
-__device__ inline uint32_t* lds_hist(SelectLds& L) { return reinterpret_cast<uint32_t*>(&L.u[kMaxK]); }
+__device__ __forceinline__ uint32_t* lds_hist(SelectLds& L) { return reinterpret_cast<uint32_t*>(&L.u[kMaxK]); }
 
 struct RowCtx {
     int64_t y;
@@ -64,12 +64,12 @@ struct RowCtx {
     const int32_t* blk_row;  // block mode: LDS copy of the row's block list
 };
 
-__device__ inline uint64_t composite(uint32_t key, int32_t idx) {
+__device__ __forceinline__ uint64_t composite(uint32_t key, int32_t idx) {
     return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
 // Key index of score column j, or -1 when the slot holds no candidate.
-__device__ inline int32_t column_index(const SelectArgs& a, const RowCtx& r, int32_t j) {
+__device__ __forceinline__ int32_t column_index(const SelectArgs& a, const RowCtx& r, int32_t j) {
     if (!a.blocks_mode) return a.col_key0 + j;
     const int32_t b = r.blk_row[j >> a.block_shift];
     if (b < 0 || r.n_tok <= 0 || b > ((r.n_tok - 1) >> a.block_shift)) return -1;
@@ -83,7 +83,7 @@ __device__ inline int32_t column_index(const SelectArgs& a, const RowCtx& r, int
 // number of times (valid = false past the end), so f may use wave-wide
 // ballots.
 template <bool VEC, int NT, class F>
-__device__ inline void visit_columns(const SelectArgs& a, const RowCtx& r, int32_t c_begin,
+__device__ __forceinline__ void visit_columns(const SelectArgs& a, const RowCtx& r, int32_t c_begin,
                                      int32_t c_end, F&& f) {
     constexpr int U = 4;
     const int tid = threadIdx.x;
@@ -123,28 +123,31 @@ __device__ inline void visit_columns(const SelectArgs& a, const RowCtx& r, int32
 }
 
 // Visit the prior list (running top-k of earlier key tiles).
+__device__ __forceinline__ int32_t prior_len(const SelectArgs& a) { return a.prior_len > 0 ? a.prior_len : a.topk; }
+
 template <int NT, class F>
-__device__ inline void visit_prior(const SelectArgs& a, const RowCtx& r, F&& f) {
+__device__ __forceinline__ void visit_prior(const SelectArgs& a, const RowCtx& r, F&& f) {
     const int tid = threadIdx.x;
     if (!r.prior) return;
-    for (int32_t base = 0; base < a.topk; base += NT) {
+    const int32_t n = prior_len(a);
+    for (int32_t base = 0; base < n; base += NT) {
         const int32_t p = base + tid;
         int32_t idx = -1;
         float v = 0.0f;
-        if (p < a.topk) {
-            idx = a.prior_idx[r.y * a.topk + p];
-            v = a.prior_val[r.y * a.topk + p];
+        if (p < n) {
+            idx = a.prior_idx[r.y * n + p];
+            v = a.prior_val[r.y * n + p];
         }
         f(idx >= 0, score_key(v), idx);
     }
 }
 
 // Wave-aggregated LDS histogram increment.
-__device__ inline void hist_add(uint32_t* h, bool valid, uint32_t bin) {
+__device__ __forceinline__ void hist_add(uint32_t* h, bool valid, uint32_t bin) {
     const uint64_t act = __ballot(valid);
     if (act == 0) return;
     const int leader = __builtin_ctzll(act);
-    const uint32_t first = (uint32_t)__shfl((int)bin, leader);
+    const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
     const uint64_t same = __ballot(valid && bin == first);
     if (same == act) {
         if ((int)(threadIdx.x & 63) == leader) atomicAdd(&h[bin], (uint32_t)__popcll(act));
@@ -154,21 +157,21 @@ __device__ inline void hist_add(uint32_t* h, bool valid, uint32_t bin) {
 }
 
 // Wave-aggregated append: returns this lane's slot (or -1 if !pred).
-__device__ inline int32_t wave_append(int32_t* counter, bool pred) {
+__device__ __forceinline__ int32_t wave_append(int32_t* counter, bool pred) {
     const uint64_t m = __ballot(pred);
     if (m == 0) return -1;
     const int lane = threadIdx.x & 63;
     const int leader = __builtin_ctzll(m);
     int32_t base = 0;
     if (lane == leader) base = atomicAdd(counter, (int32_t)__popcll(m));
-    base = __shfl(base, leader);
+    base = __builtin_amdgcn_readlane(base, leader);
     return pred ? base + (int32_t)__popcll(m & ((1ull << lane) - 1ull)) : -1;
 }
 
 // Threshold of the k best from a histogram (bins in LDS or global memory,
 // read through `get`): pick = {b*, count above b*, count in b*, total}.
 template <int NT, class G>
-__device__ inline void find_threshold(G&& get, int32_t K, int32_t* pick, int32_t* wsum) {
+__device__ __forceinline__ void find_threshold(G&& get, int32_t K, int32_t* pick, int32_t* wsum) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int kWaves = NT / kWave;
     constexpr int per = kBins / NT;  // bins per thread, descending order
@@ -218,7 +221,7 @@ __device__ inline void find_threshold(G&& get, int32_t K, int32_t* pick, int32_t
 // Sort u[0, n) descending (bitonic over the next power of two, zero padded,
 // at most cap entries).
 template <int NT>
-__device__ inline void sort_desc(uint64_t* u, int32_t n, int32_t cap) {
+__device__ __forceinline__ void sort_desc(uint64_t* u, int32_t n, int32_t cap) {
     const int tid = threadIdx.x;
     int32_t P2 = 1;
     while (P2 < n) P2 <<= 1;
@@ -244,7 +247,7 @@ __device__ inline void sort_desc(uint64_t* u, int32_t n, int32_t cap) {
 
 // Write a finished row: sel[0, n_sel) sorted descending on the composite.
 template <int NT>
-__device__ inline void write_row(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t n_sel,
+__device__ __forceinline__ void write_row(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t n_sel,
                                  bool final_out) {
     const int tid = threadIdx.x;
     uint64_t* sel = L.u;
@@ -311,10 +314,9 @@ __device__ inline void write_row(const SelectArgs& a, const RowCtx& r, SelectLds
 // scores), then an ordered scan that collects the winners.  Fills
 // L.u[0, n) and returns n.
 template <bool VEC, int NT>
-__device__ int32_t radix_fallback(const SelectArgs& a, const RowCtx& r, SelectLds& L) {
+__device__ __forceinline__ int32_t radix_fallback(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
     constexpr int kWaves = NT / kWave;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t K = a.topk;
     uint32_t* hist = reinterpret_cast<uint32_t*>(&L.u[kMaxK]);  // [kWaves][256]
     uint32_t prefix = 0;
     int shift_done = 32;
@@ -437,7 +439,7 @@ __device__ int32_t radix_fallback(const SelectArgs& a, const RowCtx& r, SelectLd
 // Finish after pass 2: sel[0, n_gt) filled; cand[0, n_cand) holds the
 // threshold bin; take its best `need`.  Returns the selected count.
 template <int NT>
-__device__ inline int32_t finish_from_candidates(SelectLds& L, int32_t n_gt, int32_t n_cand,
+__device__ __forceinline__ int32_t finish_from_candidates(SelectLds& L, int32_t n_gt, int32_t n_cand,
                                                  int32_t need) {
     const int tid = threadIdx.x;
     uint64_t* cand = &L.u[kMaxK];
@@ -450,7 +452,7 @@ __device__ inline int32_t finish_from_candidates(SelectLds& L, int32_t n_gt, int
 }
 
 template <int NT>
-__device__ inline void setup_row(const SelectArgs& a, RowCtx& r, SelectLds& L, int64_t y,
+__device__ __forceinline__ void setup_row(const SelectArgs& a, RowCtx& r, SelectLds& L, int64_t y,
                                  int32_t& count) {
     const int tid = threadIdx.x;
     r.y = y;
@@ -475,6 +477,51 @@ __device__ inline void setup_row(const SelectArgs& a, RowCtx& r, SelectLds& L, i
 
 // ------------------------------------------------- one workgroup per row
 
+// Exact selection of the row's top-K candidates into L.u[0, n) (unsorted);
+// returns n.
+template <bool VEC, int NT>
+__device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
+    const int tid = threadIdx.x;
+    if (K <= 0) return 0;
+    uint32_t* hist = lds_hist(L);
+    // pass 1: 12-bit histogram
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    auto h = [&](bool valid, uint32_t key, int32_t) { hist_add(hist, valid, key >> kBinShift); };
+    visit_prior<NT>(a, r, h);
+    visit_columns<VEC, NT>(a, r, r.lo, r.hi, h);
+    __syncthreads();
+    find_threshold<NT>([&](int b) { return hist[b]; }, K, L.pick, L.wsum);
+    const int32_t bstar = L.pick[0];
+    const int32_t above = L.pick[1], inbin = L.pick[2], total = L.pick[3];
+    __syncthreads();
+    if (bstar >= 0 && inbin > kCap && inbin != K - above) return radix_fallback<VEC, NT>(a, r, L, K);
+    // pass 2: collect
+    const bool all = bstar < 0;  // total <= K
+    const bool whole_bin = !all && inbin == K - above;
+    if (tid == 0) {
+        L.cnt[0] = 0;
+        L.cnt[1] = 0;
+    }
+    __syncthreads();
+    auto c = [&](bool valid, uint32_t key, int32_t idx) {
+        const uint32_t bin = key >> kBinShift;
+        const bool to_sel =
+            valid && (all || (int32_t)bin > bstar || (whole_bin && (int32_t)bin == bstar));
+        const bool to_cand = valid && !all && !whole_bin && (int32_t)bin == bstar;
+        const int32_t ps = wave_append(&L.cnt[0], to_sel);
+        if (to_sel && ps < kMaxK) L.u[ps] = composite(key, idx);
+        const int32_t pc = wave_append(&L.cnt[1], to_cand);
+        if (to_cand && pc < kCap) L.u[kMaxK + pc] = composite(key, idx);
+    };
+    visit_prior<NT>(a, r, c);
+    visit_columns<VEC, NT>(a, r, r.lo, r.hi, c);
+    __syncthreads();
+    if (all) return total;
+    if (whole_bin) return K;
+    return finish_from_candidates<NT>(L, above, inbin, K - above);
+}
+
 template <bool VEC, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows) {
     __shared__ SelectLds L;
@@ -486,55 +533,64 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     if (!a.always_final && a.tile_begin > 0 && count <= a.tile_begin) return;
     const bool final_out = a.always_final || count <= a.tile_end;
     const int32_t K = a.topk;
-    uint32_t* hist = lds_hist(L);
 
-    int32_t n_sel = 0;
-    if (K > 0) {
-        // pass 1: 12-bit histogram
-        for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    if (a.part_span > 0) {
+        // stage A: the best K of one column partition
+        const int32_t p = blockIdx.y;
+        const int32_t c0 = r.lo + p * a.part_span;
+        const int32_t c1 = min(r.hi, c0 + a.part_span);
+        r.lo = c0;
+        r.hi = max(c0, c1);
+        const int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
         __syncthreads();
-        auto h = [&](bool valid, uint32_t key, int32_t) { hist_add(hist, valid, key >> kBinShift); };
-        visit_prior<NT>(a, r, h);
-        visit_columns<VEC, NT>(a, r, r.lo, r.hi, h);
-        __syncthreads();
-        find_threshold<NT>([&](int b) { return hist[b]; }, K, L.pick, L.wsum);
-        const int32_t bstar = L.pick[0];
-        const int32_t above = L.pick[1], inbin = L.pick[2], total = L.pick[3];
-        __syncthreads();
-        if (bstar >= 0 && inbin > kCap && inbin != K - above) {
-            n_sel = radix_fallback<VEC, NT>(a, r, L);
-        } else {
-            // pass 2: collect
-            const bool all = bstar < 0;                    // total <= K
-            const bool whole_bin = !all && inbin == K - above;
-            if (tid == 0) {
-                L.cnt[0] = 0;
-                L.cnt[1] = 0;
+        sort_desc<NT>(L.u, n_sel, kMaxK);
+        const int64_t o = r.y * (int64_t)a.run_stride + (int64_t)p * K;
+        for (int j = tid; j < K; j += NT) {
+            int32_t id = -1;
+            float v = __builtin_nanf("");
+            if (j < n_sel) {
+                const uint64_t cc = L.u[j];
+                id = (int32_t)(0xFFFFFFFFu - (uint32_t)cc);
+                v = key_score((uint32_t)(cc >> 32));
             }
-            __syncthreads();
-            auto c = [&](bool valid, uint32_t key, int32_t idx) {
-                const uint32_t bin = key >> kBinShift;
-                const bool to_sel = valid && (all || (int32_t)bin > bstar ||
-                                              (whole_bin && (int32_t)bin == bstar));
-                const bool to_cand = valid && !all && !whole_bin && (int32_t)bin == bstar;
-                const int32_t ps = wave_append(&L.cnt[0], to_sel);
-                if (to_sel && ps < kMaxK) L.u[ps] = composite(key, idx);
-                const int32_t pc = wave_append(&L.cnt[1], to_cand);
-                if (to_cand && pc < kCap) L.u[kMaxK + pc] = composite(key, idx);
-            };
-            visit_prior<NT>(a, r, c);
-            visit_columns<VEC, NT>(a, r, r.lo, r.hi, c);
-            __syncthreads();
-            if (all)
-                n_sel = total;
-            else if (whole_bin)
-                n_sel = K;
-            else
-                n_sel = finish_from_candidates<NT>(L, above, inbin, K - above);
+            a.run_idx[o + j] = id;
+            a.run_val[o + j] = v;
         }
+        if (tid == 0) a.part_cnt[r.y * gridDim.y + p] = r.hi - r.lo;
+        return;
     }
+
+    // stage B merges the partial lists (prior) without the score columns
+    const int32_t col_lo = r.lo, col_hi = r.hi;
+    if (a.parts > 0) r.hi = r.lo;
+    int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
     __syncthreads();
     sort_desc<NT>(L.u, n_sel, kMaxK);
+    if (a.parts > 0) {
+        // exact iff every truncated partition's last kept candidate ranks
+        // no higher than the merged k-th (dropped candidates rank below it)
+        if (tid == 0) L.cnt[0] = 0;
+        __syncthreads();
+        const uint64_t kth = n_sel == K ? L.u[K - 1] : 0;
+        const int32_t n = prior_len(a);
+        for (int p = tid; p < a.parts; p += NT) {
+            if (a.part_cnt[r.y * a.parts + p] > a.part_k) {
+                const int64_t o = r.y * (int64_t)n + (int64_t)p * a.part_k + a.part_k - 1;
+                const uint64_t cut = composite(score_key(a.prior_val[o]), a.prior_idx[o]);
+                if (n_sel < K || cut > kth) L.cnt[0] = 1;
+            }
+        }
+        __syncthreads();
+        if (L.cnt[0]) {
+            r.prior = false;
+            r.lo = col_lo;
+            r.hi = col_hi;
+            __syncthreads();
+            n_sel = select_core<VEC, NT>(a, r, L, K);
+            __syncthreads();
+            sort_desc<NT>(L.u, n_sel, kMaxK);
+        }
+    }
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
@@ -543,13 +599,11 @@ bool vec_ok(const SelectArgs& a) {
 }
 
 template <int NT>
-void launch_nt(const SelectArgs& a, int64_t n_rows, hipStream_t stream) {
+void launch_nt(const SelectArgs& a, int64_t n_rows, dim3 grid, hipStream_t stream) {
     if (vec_ok(a))
-        hipLaunchKernelGGL((select_kernel<true, NT>), dim3((unsigned)n_rows), dim3(NT), 0, stream,
-                           a, n_rows);
+        hipLaunchKernelGGL((select_kernel<true, NT>), grid, dim3(NT), 0, stream, a, n_rows);
     else
-        hipLaunchKernelGGL((select_kernel<false, NT>), dim3((unsigned)n_rows), dim3(NT), 0, stream,
-                           a, n_rows);
+        hipLaunchKernelGGL((select_kernel<false, NT>), grid, dim3(NT), 0, stream, a, n_rows);
 }
 
 }  // namespace
@@ -558,9 +612,64 @@ hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream
     if (n_rows <= 0) return hipSuccess;
     // few rows: a wide workgroup per row; many rows: several narrow ones per CU
     if (n_rows < 512)
-        launch_nt<1024>(a, n_rows, stream);
+        launch_nt<1024>(a, n_rows, dim3((unsigned)n_rows), stream);
     else
-        launch_nt<256>(a, n_rows, stream);
+        launch_nt<256>(a, n_rows, dim3((unsigned)n_rows), stream);
+    return hipGetLastError();
+}
+
+SelectSplit select_split(int64_t n_rows, int32_t n_cols, int32_t topk) {
+    SelectSplit sp{0, 0, 0};
+    constexpr int32_t span = 4096;
+    // one 1024-thread workgroup per row keeps up with rows up to ~64K
+    // candidates; longer rows spread over several CUs
+    if (n_rows <= 0 || n_rows >= 512 || n_cols < 32 * span) return sp;
+    const int32_t parts = (n_cols + span - 1) / span;
+    // twice the expected share of each partition, as a power of two
+    int32_t kp = 64;
+    while (kp < 2 * ((topk + parts - 1) / parts)) kp <<= 1;
+    kp = std::min(kp, topk);
+    if ((int64_t)parts * kp < topk) return sp;
+    sp.parts = parts;
+    sp.span = span;
+    sp.part_k = kp;
+    return sp;
+}
+
+size_t select_split_workspace(int64_t n_rows, const SelectSplit& sp) {
+    if (sp.parts == 0) return 0;
+    const int64_t list = n_rows * sp.parts * (int64_t)sp.part_k;
+    return (size_t)((list * 8 + n_rows * sp.parts * 4 + 255) / 256 * 256);
+}
+
+hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const SelectSplit& sp,
+                               void* ws, hipStream_t stream) {
+    if (n_rows <= 0) return hipSuccess;
+    const int64_t list = n_rows * sp.parts * (int64_t)sp.part_k;
+    float* pv = static_cast<float*>(ws);
+    int32_t* pi = reinterpret_cast<int32_t*>(pv + list);
+    int32_t* pc = pi + list;
+    SelectArgs sa = a;  // stage A
+    sa.topk = sp.part_k;
+    sa.part_span = sp.span;
+    sa.run_stride = sp.parts * sp.part_k;
+    sa.run_val = pv;
+    sa.run_idx = pi;
+    sa.part_cnt = pc;
+    sa.prior_val = nullptr;
+    sa.prior_idx = nullptr;
+    sa.always_final = 1;
+    launch_nt<256>(sa, n_rows, dim3((unsigned)n_rows, (unsigned)sp.parts), stream);
+    SelectArgs sb = a;  // stage B
+    sb.prior_val = pv;
+    sb.prior_idx = pi;
+    sb.prior_len = sp.parts * sp.part_k;
+    sb.tile_begin = 1;  // use the prior list
+    sb.always_final = 1;
+    sb.parts = sp.parts;
+    sb.part_k = sp.part_k;
+    sb.part_cnt = pc;
+    launch_nt<1024>(sb, n_rows, dim3((unsigned)n_rows), stream);
     return hipGetLastError();
 }
 

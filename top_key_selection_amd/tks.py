@@ -269,7 +269,8 @@ def hisa_topk(shape: Shape, q, w, k, k_scale, block, m_scored, force_flags, topk
     return idx, vals, blk
 
 
-PROFILE_ROLES = ("score_flat", "score_pooled", "score_refine", "select", "pool")
+PROFILE_ROLES = ("score_flat", "score_pooled", "score_refine", "select_flat", "select_pooled",
+                 "select_refine", "select_scores", "pool")
 
 
 def profile_enable(on: bool = True):
