@@ -55,8 +55,9 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a, int64_t n_bl
             const int64_t b2 = bj0 + gg;
             if (b2 < n_blocks) {
                 const int64_t row0 = (b2 / nb) * a.n_k + (b2 % nb) * a.block + c0;
-                const u32x4 x = *reinterpret_cast<const u32x4*>(
-                    reinterpret_cast<const uint8_t*>(a.k) + row0 * ROW + off);
+                // each block chunk is contiguous: whole lines, streamed once
+                const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                    reinterpret_cast<const uint8_t*>(a.k) + row0 * ROW + off));
                 *reinterpret_cast<u32x4*>(&s_keys[gg * STRIDE + off]) = x;
             }
         }

@@ -246,43 +246,44 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
 
 template <int D>
 struct Fp8Ring {
-    static constexpr int R = 4;                       // stages in flight per wave
+    static constexpr int R = 3;                       // stages in flight per wave
     static constexpr int CH = D / 32;                 // 16-byte chunks per lane and key
     static constexpr int STAGE = CH * 1024 + 256;     // chunk slabs + per-lane scales
     static constexpr int WAVE = R * STAGE;
 };
 
-// Read one ring stage (CH 16-byte chunks 1 KiB apart, and the scale) with a
-// single wait; early-clobber outputs keep every address register intact
-// while the reads are in flight.
+// Read one ring stage (CH 16-byte chunks at base + off[c], and the scale)
+// with a single wait; early-clobber outputs keep every address register
+// intact while the reads are in flight.
 template <int CH>
-__device__ __forceinline__ void lds_read_stage(uint32_t addr, uint32_t saddr, u32x4* raw,
-                                               float& scale) {
+__device__ __forceinline__ void lds_read_stage(uint32_t base, const uint32_t* off, uint32_t saddr,
+                                               u32x4* raw, float& scale) {
     if constexpr (CH == 4) {
         asm volatile(
             "ds_read_b128 %0, %5\n\t"
-            "ds_read_b128 %1, %5 offset:1024\n\t"
-            "ds_read_b128 %2, %5 offset:2048\n\t"
-            "ds_read_b128 %3, %5 offset:3072\n\t"
-            "ds_read_b32 %4, %6\n\t"
+            "ds_read_b128 %1, %6\n\t"
+            "ds_read_b128 %2, %7\n\t"
+            "ds_read_b128 %3, %8\n\t"
+            "ds_read_b32 %4, %9\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(scale)
-            : "v"(addr), "v"(saddr));
+            : "v"(base + off[0]), "v"(base + off[1]), "v"(base + off[2]), "v"(base + off[3]),
+              "v"(saddr));
     } else if constexpr (CH == 2) {
         asm volatile(
             "ds_read_b128 %0, %3\n\t"
-            "ds_read_b128 %1, %3 offset:1024\n\t"
-            "ds_read_b32 %2, %4\n\t"
+            "ds_read_b128 %1, %4\n\t"
+            "ds_read_b32 %2, %5\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(scale)
-            : "v"(addr), "v"(saddr));
+            : "v"(base + off[0]), "v"(base + off[1]), "v"(saddr));
     } else {
         asm volatile(
             "ds_read_b128 %0, %2\n\t"
             "ds_read_b32 %1, %3\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(raw[0]), "=&v"(scale)
-            : "v"(addr), "v"(saddr));
+            : "v"(base + off[0]), "v"(saddr));
     }
 }
 
@@ -299,6 +300,8 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     using RG = Fp8Ring<D>;
     constexpr int KS = D / 16;
     __shared__ __align__(16) uint8_t ring[4 * RG::WAVE];
+    __shared__ __align__(16) uint16_t s_q[MB * 32 * D];  // the row's q, zero-padded heads
+    __shared__ float s_w[MB * 32];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m = lane & 31;
@@ -316,27 +319,8 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     const int32_t work_end = a.write_masked ? slot_end : limit;
     if (slot_begin >= work_end) return;
 
-    bf16x8 qa[MB][KS];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int h = mb * 32 + m;
-        const int hc = h < a.heads ? h : 0;
-        const u32x4* p = reinterpret_cast<const u32x4*>(a.q + (qr * a.heads + hc) * D + hf * (D / 2));
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = p[ks];
-            qa[mb][ks] = __builtin_bit_cast(bf16x8, h < a.heads ? v : u32x4{0, 0, 0, 0});
-        }
-    }
+    bf16x8 qa[MB][KS];  // loaded after the first ring copies are issued
     float wv[MB][16];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int h = mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
-            wv[mb][j] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
-        }
-
     const int64_t kseq = (int64_t)seq * a.k_seq_len;
     const int32_t* blk_row = BLOCKS ? a.blk + (a.rows.y0 + y) * a.blk_stride : nullptr;
     const int32_t bmask = (1 << a.block_shift) - 1;
@@ -358,24 +342,59 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     const int32_t first = slot_begin + wave * 32;
     const int32_t nsub = first < work_end ? (work_end - first + 127) / 128 : 0;
 
+    // D = 128: copy instruction c reads key rows 8c .. 8c+7 of the sub-block
+    // as one contiguous KiB (full cache lines, nontemporal): lane j = 8r + q
+    // takes chunk (q - r - c) mod 8 of row 8c + r.  The read-back below
+    // inverts the rotation, which spreads every 16-lane group of a read over
+    // all LDS banks.  Other dims copy each lane's own half row.
+    constexpr bool ROT = D == 128;
+    const int rr = lane >> 3, qq = lane & 7;
     auto fetch = [&](int32_t u) {
-        bool valid;
-        const int32_t key = key_of(first + u * 128 + m, valid);
-        const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k) + row * D + hf * (D / 2);
         uint8_t* st = wring + (u % RG::R) * RG::STAGE;
+        if constexpr (ROT) {
 #pragma unroll
-        for (int c = 0; c < RG::CH; ++c)
-            __builtin_amdgcn_global_load_lds(src + c * 16, st + c * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.k_scale + row, st + RG::CH * 1024, 4, 0, 0);
+            for (int c = 0; c < RG::CH; ++c) {
+                bool valid;
+                const int32_t key = key_of(first + u * 128 + 8 * c + rr, valid);
+                const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+                const int chunk = (qq - rr - c) & 7;
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const uint8_t*>(a.k) + row * D + chunk * 16, st + c * 1024,
+                    16, 0, 2);
+            }
+            bool valid;
+            const int32_t key = key_of(first + u * 128 + m, valid);
+            const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+            __builtin_amdgcn_global_load_lds(a.k_scale + row, st + RG::CH * 1024, 4, 0, 0);
+        } else {
+            bool valid;
+            const int32_t key = key_of(first + u * 128 + m, valid);
+            const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k) + row * D + hf * (D / 2);
+#pragma unroll
+            for (int c = 0; c < RG::CH; ++c)
+                __builtin_amdgcn_global_load_lds(src + c * 16, st + c * 1024, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.k_scale + row, st + RG::CH * 1024, 4, 0, 0);
+        }
     };
+    // read-back offsets of this lane's four chunks (key m, half hf)
+    uint32_t roff[RG::CH];
+#pragma unroll
+    for (int c = 0; c < RG::CH; ++c) {
+        if constexpr (ROT) {
+            const int i = m >> 3, r = m & 7, cc = hf * 4 + c;
+            roff[c] = i * 1024 + (8 * r + ((cc + r + i) & 7)) * 16;
+        } else {
+            roff[c] = c * 1024 + lane * 16;
+        }
+    }
 
     // MFMAs of sub-block u, from the ring slot it occupies
     auto mfma_stage = [&](int32_t u, f32x16* acc, float& scale) {
         wait_vmcnt<(RG::R - 1) * (RG::CH + 1)>();
         const uint32_t st = wring_addr + (u % RG::R) * RG::STAGE;
         u32x4 raw[RG::CH];
-        lds_read_stage<RG::CH>(st + lane * 16, st + RG::CH * 1024 + lane * 4, raw, scale);
+        lds_read_stage<RG::CH>(st, roff, st + RG::CH * 1024 + lane * 4, raw, scale);
         fetch(u + RG::R);  // refill the slot just read
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -421,6 +440,32 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
 
 #pragma unroll
     for (int u = 0; u < RG::R; ++u) fetch(u);
+    // q / w: read once per workgroup into LDS (overlapping the first ring
+    // copies), then every wave builds its fragments from there
+    {
+        const int hq = a.heads * D;  // bf16 elements of the row's q
+        const uint16_t* qsrc = a.q + qr * hq;
+        for (int e = threadIdx.x * 8; e < MB * 32 * D; e += 256 * 8) {
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (e < hq) v = *reinterpret_cast<const u32x4*>(qsrc + e);
+            *reinterpret_cast<u32x4*>(&s_q[e]) = v;
+        }
+        for (int h = threadIdx.x; h < MB * 32; h += 256) s_w[h] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int h = mb * 32 + m;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qa[mb][ks] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(&s_q[h * D + hf * (D / 2) + ks * 8]));
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wv[mb][j] = s_w[mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3)];
+
     // two accumulator sets: the MFMAs of sub-block u + 1 are issued before the
     // VALU epilogue of sub-block u, so the matrix and vector pipes overlap
     f32x16 acc0[MB], acc1[MB];
@@ -442,8 +487,8 @@ hipError_t launch_t(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
     if (FP8 && a.stream_keys) {
         // keys read once: fp8 LDS-ring streaming kernel, >= ~2048 workgroups
-        // about two long-lived workgroups per CU: each loads its row's q / w
-        // once and streams a long run of keys
+        // about two long-lived workgroups per CU, each loading its row's q / w
+        // once and streaming a long run of keys
         const int64_t want = (n_rows * (int64_t)a.n_cols + 511) / 512;
         int64_t seg = std::min<int64_t>(16384, std::max<int64_t>(128, (want + 127) / 128 * 128));
         while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
