@@ -202,6 +202,55 @@ def test_head_and_dim_variants_exact(heads, dim):
     assert_topk_exact(gi, gv, oi, ov, "heads/dim")
 
 
+@pytest.mark.parametrize("q_chunk,k_tile", [(0, 0), (100, 192), (37, 64), (613, 1024)])
+def test_shared_key_prefill_path_exact(q_chunk, k_tile):
+    """Prefill with D = 128: blocks of consecutive queries of one sequence
+    share staged key tiles.  Ragged sequence lengths, chunks that straddle
+    sequence boundaries and tiles of a few stages must still give the oracle's
+    exact result."""
+    say("shared-key prefill q_chunk=%d k_tile=%d" % (q_chunk, k_tile))
+    sh, x = int_case(60, batch=3, n_q=203, n_k=1500, heads=64, dim=128, q_pos0=1297, lo=-2, hi=2)
+    oi, ov = _cached_oracle(("shared",), sh, x, 300)
+    gi, gv = gpu_flat(sh, x, 300, q_chunk, k_tile)
+    assert_topk_exact(gi, gv, oi, ov, "shared prefill")
+
+
+def test_shared_key_scores_and_ratio_exact():
+    """indexer_scores rectangles (masked slots written as -inf) and
+    compressed causality through the shared-key scoring path."""
+    say("shared-key scores rectangles, ratio 4")
+    sh, x = int_case(61, batch=2, n_q=300, n_k=800, heads=64, dim=128, q_pos0=-9, ratio=4,
+                     lo=-2, hi=2)
+    q, w, k, ks = gpu_inputs(x)
+    for (q0, qn, k0, kn) in [(0, 300, 0, 800), (11, 77, 3, 129), (290, 10, 0, 75)]:
+        got = host(tks.indexer_scores(tks.Shape(**sh), q, w, k, ks, q0, qn, k0, kn))
+        ref = oracle.index_scores(sh, x["q"], x["w"], x["k"], None, q0, qn, k0, kn)
+        np.testing.assert_array_equal(got.astype(np.float64), ref)
+    oi, ov = oracle_flat(sh, x, 40)
+    gi, gv = gpu_flat(sh, x, 40)
+    assert_topk_exact(gi, gv, oi, ov, "shared ratio")
+
+
+def test_shared_key_hisa_prefill_exact():
+    """HISA prefill with D = 128: pooled-block scoring runs on the shared-key
+    path and refinement on the gathered path; blocks and tokens must equal
+    the oracle's."""
+    say("HISA prefill D=128 block 64 m 5")
+    sh, x = int_case(62, batch=2, n_q=600, n_k=1200, heads=64, dim=128, q_pos0=600, lo=-2, hi=2)
+    R = 1200
+    rows = np.arange(R)
+    qr, wr = x["q"].reshape(R, 64, 128), x["w"].reshape(R, 64)
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, 64, 5, FORCE_FIRST | FORCE_LOCAL,
+                                      256, rows)
+    q, w, k, ks = gpu_inputs(x)
+    idx, vals, blk = tks.hisa_topk(tks.Shape(**sh), q, w, k, ks, 64, 5, FORCE_FIRST | FORCE_LOCAL,
+                                   256)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                      "shared hisa")
+
+
 def test_fp8_keys_integer_exact():
     say("fp8 keys, integer codes, power-of-two scales")
     sh, x = int_case(28, batch=2, n_q=64, n_k=1100, heads=8, dim=128, q_pos0=1036, fp8=True)

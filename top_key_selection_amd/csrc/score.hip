@@ -482,9 +482,248 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     wait_vmcnt<0>();
 }
 
+// ------------------------------------------------------------------------
+// Keys shared by a block of queries (prefill: contiguous key runs, bf16
+// keys, D = 128).  A workgroup of NW waves owns NW consecutive query rows
+// of one sequence, one row per wave, and a run of key slots.  The run is
+// staged through an LDS ring of 64-key stages that all waves fill together
+// with direct global->LDS copies; every staged key feeds the MFMAs of all NW
+// queries, so a key crosses the L2 once per NW queries instead of once per
+// query, and the copies run NS - 1 stages ahead of the MFMAs.
+//
+// Stage layout: key row r (256 bytes = 16 chunks of 16 bytes) keeps logical
+// chunk c at physical chunk c ^ (r & 15).  A copy writes LDS linearly (lane
+// i lands at base + 16 i), so each lane fetches the global chunk that
+// belongs at its position; one copy still covers 4 whole key rows (1 KiB
+// contiguous in memory).  When the lanes holding keys 0..31 read logical
+// chunk c, every 16 consecutive lanes touch 16 distinct chunk columns, so
+// the reads are free of bank conflicts.
+struct SharedRing {
+    static constexpr int D = 128;
+    static constexpr int SK = 64;            // keys per stage
+    static constexpr int STAGE = SK * D * 2;  // 16 KiB
+    static constexpr int NS = 3;              // stages in flight
+};
+constexpr int kSharedRows = 8;  // query rows (waves) per workgroup
+
+// Lanes 0-31 get x + x[lane + 32] (v_permlane32_swap: its second result
+// holds the upper half's values in the lower half).  The builtin exists for
+// the device pass only.
+__device__ __forceinline__ float add_upper_half(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                     false);
+    return x + __uint_as_float(sw[1]);
+#else
+    return x;
+#endif
+}
+
+// Read the 8 B-operand chunks of one 32-key sub-block with a single wait.
+__device__ __forceinline__ void lds_read_sub(uint32_t base, const uint32_t* off, u32x4* raw) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(raw[4]),
+          "=&v"(raw[5]), "=&v"(raw[6]), "=&v"(raw[7])
+        : "v"(base + off[0]), "v"(base + off[1]), "v"(base + off[2]), "v"(base + off[3]),
+          "v"(base + off[4]), "v"(base + off[5]), "v"(base + off[6]), "v"(base + off[7]));
+}
+
+template <int MB, int NW>
+__global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int64_t n_rows,
+                                                               int32_t blocks_per_seq,
+                                                               int32_t seg_slots) {
+    using RG = SharedRing;
+    constexpr int D = RG::D;
+    constexpr int KS = D / 16;
+    constexpr int CPW = RG::STAGE / (NW * 64 * 16);  // copies per wave and stage
+    static_assert(CPW * NW * 64 * 16 == RG::STAGE, "stage split");
+    __shared__ __align__(16) uint8_t ring[RG::NS * RG::STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int hf = lane >> 5;
+
+    // chunk rows [r_lo, r_hi) of one sequence
+    const int64_t R = a.rows.rows_per_seq;
+    const int64_t seq = a.rows.y0 / R + blockIdx.x / blocks_per_seq;
+    const int64_t s_lo = seq * R - a.rows.y0;
+    const int64_t lo = s_lo > 0 ? s_lo : 0;
+    const int64_t hi = s_lo + R < n_rows ? s_lo + R : n_rows;
+    const int64_t r_lo = lo + (int64_t)(blockIdx.x % blocks_per_seq) * NW;
+    if (r_lo >= hi) return;
+    const int64_t r_hi = r_lo + NW < hi ? r_lo + NW : hi;
+    const bool active = r_lo + wave < r_hi;
+    const int64_t y = active ? r_lo + wave : r_hi - 1;  // idle waves shadow the last row
+    const int32_t t = a.rows.query(y);
+    const int64_t qr = a.rows.qrow(y);
+
+    const int32_t slot_begin = blockIdx.y * seg_slots;
+    const int32_t slot_end = min(a.n_cols, slot_begin + seg_slots);
+    // visibility grows with the query: the block's last row sees the most
+    const int32_t blk_limit =
+        min(slot_end, max(0, a.vis.count(a.rows.query(r_hi - 1)) - a.col_key0));
+    const int32_t work_end = a.write_masked ? slot_end : blk_limit;
+    if (slot_begin >= work_end) return;
+    const int32_t limit = min(slot_end, max(0, a.vis.count(t) - a.col_key0));
+    const int32_t n_st = (work_end - slot_begin + RG::SK - 1) / RG::SK;
+    const int32_t nsub = (work_end - slot_begin + 31) / 32;
+
+    // q fragment and head weights (as in score_kernel)
+    bf16x8 qa[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int h = mb * 32 + m;
+        if (h < a.heads) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(a.q + (qr * a.heads + h) * D + hf * (D / 2));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, p[ks]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        }
+    }
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int h = mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
+            wv[mb][j] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+        }
+
+    // copies: chunk p = (i * NW + wave) * 64 + lane of a stage is row p / 16,
+    // physical chunk p % 16, logical chunk (p % 16) ^ (row & 15)
+    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k) + seq * a.k_seq_len * (2 * D);
+    const int32_t kmax = (int32_t)(a.k_seq_len - 1);
+    int32_t crow[CPW];
+    uint32_t cchunk[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int p = (i * NW + wave) * 64 + lane;
+        crow[i] = p >> 4;
+        cchunk[i] = (uint32_t)(((p & 15) ^ ((p >> 4) & 15)) * 16);
+    }
+    auto fetch = [&](int32_t s) {
+        uint8_t* st = ring + (s % RG::NS) * RG::STAGE;
+        const int32_t key0 = a.col_key0 + slot_begin + s * RG::SK;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int32_t key = min(key0 + crow[i], kmax);
+            // (one 64-bit offset: with two separate additions the host pass
+            // of this compiler drops the kernel's launch stub)
+            __builtin_amdgcn_global_load_lds(kseq + ((int64_t)key * (2 * D) + (int64_t)cchunk[i]),
+                                             st + (i * NW + wave) * 1024, 16, 0, 0);
+        }
+    };
+    // Stage s is ready once this wave's copies of it have landed (copies of
+    // one wave complete in order; the later stages already issued, and any
+    // stores, only raise the count) and every wave has passed the barrier,
+    // which also means all waves are done reading stage s - 1, whose slot
+    // the next copy reuses.
+    auto sync = [&](int32_t s) {
+        if (s + 1 < n_st)
+            wait_vmcnt<CPW * (RG::NS - 2)>();
+        else
+            wait_vmcnt<0>();
+        asm volatile("s_barrier" ::: "memory");
+        if (s + RG::NS - 1 < n_st) fetch(s + RG::NS - 1);
+    };
+    static_assert(RG::NS == 3, "sync() counts one later stage");
+
+    uint32_t roff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = m * (2 * D) + (((hf * 8 + ks) ^ (m & 15)) * 16);
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    auto mfma_sub = [&](int32_t u, f32x16* acc) {
+        u32x4 raw[KS];
+        lds_read_sub(ring_addr + ((u >> 1) % RG::NS) * RG::STAGE + (u & 1) * 32 * (2 * D), roff, raw);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, raw[ks]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+        }
+    };
+    auto reduce = [&](const f32x16* acc) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
+        return add_upper_half(sc);
+    };
+    float* orow = a.out + y * a.out_stride;
+    auto store = [&](int32_t u, float sc) {
+        const int32_t slot = slot_begin + u * 32 + m;
+        if (active && hf == 0 && slot < slot_end) {
+            if (slot < limit)
+                orow[slot] = sc;
+            else if (a.write_masked)
+                orow[slot] = -__builtin_inff();
+        }
+    };
+
+#pragma unroll
+    for (int s = 0; s < RG::NS - 1; ++s)
+        if (s < n_st) fetch(s);
+    // sub-block u is the (u & 1) half of stage u / 2.  The MFMAs of u + 1 are
+    // issued before the VALU reduction of u (two accumulator sets), and the
+    // store of an even sub-block waits until after the next barrier so that
+    // the stage waits never cover a store just issued.
+    f32x16 acc0[MB], acc1[MB];
+    sync(0);
+    mfma_sub(0, acc0);
+    for (int32_t u = 0; u < nsub; u += 2) {
+        if (u + 1 < nsub) mfma_sub(u + 1, acc1);
+        const float s0 = reduce(acc0);
+        if (u + 2 < nsub) {
+            sync((u + 2) >> 1);
+            store(u, s0);
+            mfma_sub(u + 2, acc0);
+        } else {
+            store(u, s0);
+        }
+        if (u + 1 < nsub) store(u + 1, reduce(acc1));
+    }
+    wait_vmcnt<0>();
+}
+
+template <int MB, int NW>
+hipError_t launch_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
+    const int64_t R = a.rows.rows_per_seq;
+    const int64_t n_seq = (a.rows.y0 + n_rows - 1) / R - a.rows.y0 / R + 1;
+    const int64_t per_seq = (std::min<int64_t>(n_rows, R) + NW - 1) / NW;
+    // segments: a multiple of the stage, sized for a few workgroups per CU
+    const int64_t want = n_rows * (int64_t)a.n_cols / (NW * 4096);
+    int64_t seg = std::min<int64_t>(4096, std::max<int64_t>(512, (want + 63) / 64 * 64));
+    while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
+    dim3 grid((unsigned)(n_seq * per_seq), (unsigned)((a.n_cols + seg - 1) / seg));
+    hipLaunchKernelGGL((score_shared_kernel<MB, NW>), grid, dim3(NW * 64), 0, stream, a, n_rows,
+                       (int32_t)per_seq, (int32_t)seg);
+    return hipGetLastError();
+}
+
 template <int D, int MB, bool FP8, bool BLOCKS>
 hipError_t launch_t(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
+    // several queries of one sequence per workgroup share each key tile
+    if (D == 128 && !FP8 && !BLOCKS && !a.stream_keys && a.k_seq_len > 0 &&
+        std::min<int64_t>(n_rows, a.rows.rows_per_seq) >= kSharedRows)
+        return launch_shared<MB, kSharedRows>(a, n_rows, stream);
     if (FP8 && a.stream_keys) {
         // keys read once: fp8 LDS-ring streaming kernel, >= ~2048 workgroups
         // about two long-lived workgroups per CU, each loading its row's q / w
