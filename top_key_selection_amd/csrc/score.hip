@@ -501,6 +501,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
 struct SharedRing {
     static constexpr int D = 128;
     static constexpr int SK = 64;            // keys per stage
+    static constexpr int SPS = SK / 32;       // 32-key sub-blocks per stage
     static constexpr int STAGE = SK * D * 2;  // 16 KiB
     static constexpr int NS = 3;              // stages in flight
 };
@@ -563,14 +564,15 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
     const int64_t r_hi = r_lo + NW < hi ? r_lo + NW : hi;
     const bool active = r_lo + wave < r_hi;
     const int64_t y = active ? r_lo + wave : r_hi - 1;  // idle waves shadow the last row
-    const int32_t t = a.rows.query(y);
-    const int64_t qr = a.rows.qrow(y);
+    // (the RowMap helpers without their 64-bit divisions: seq is known)
+    const int32_t t = a.rows.t_begin + (int32_t)(y - s_lo);
+    const int64_t qr = seq * a.rows.n_q + t;
 
     const int32_t slot_begin = blockIdx.y * seg_slots;
     const int32_t slot_end = min(a.n_cols, slot_begin + seg_slots);
     // visibility grows with the query: the block's last row sees the most
     const int32_t blk_limit =
-        min(slot_end, max(0, a.vis.count(a.rows.query(r_hi - 1)) - a.col_key0));
+        min(slot_end, max(0, a.vis.count(a.rows.t_begin + (int32_t)(r_hi - 1 - s_lo)) - a.col_key0));
     const int32_t work_end = a.write_masked ? slot_end : blk_limit;
     if (slot_begin >= work_end) return;
     const int32_t limit = min(slot_end, max(0, a.vis.count(t) - a.col_key0));
@@ -638,6 +640,7 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
         if (s + RG::NS - 1 < n_st) fetch(s + RG::NS - 1);
     };
     static_assert(RG::NS == 3, "sync() counts one later stage");
+    static_assert(RG::SPS % 2 == 0, "sub-block pairs never straddle a stage");
 
     uint32_t roff[KS];
 #pragma unroll
@@ -645,7 +648,8 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
     const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
     auto mfma_sub = [&](int32_t u, f32x16* acc) {
         u32x4 raw[KS];
-        lds_read_sub(ring_addr + ((u >> 1) % RG::NS) * RG::STAGE + (u & 1) * 32 * (2 * D), roff, raw);
+        lds_read_sub(ring_addr + ((u / RG::SPS) % RG::NS) * RG::STAGE + (u % RG::SPS) * 32 * (2 * D),
+                     roff, raw);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -666,6 +670,35 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
             for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
         return add_upper_half(sc);
     };
+    // MFMAs of sub-block u into `acc`, with the ReLU * w reduction of the
+    // previous sub-block (`prev`) spread between them in program order: each
+    // k-step's MFMAs are followed by the next slice of the reduction, fenced
+    // so the scheduler keeps the interleave and the vector work issues while
+    // the matrix pipe is busy.  The reduction order is that of reduce().
+    auto mfma_reduce = [&](int32_t u, f32x16* acc, const f32x16* prev) {
+        constexpr int PER = MB * 16 / KS;  // reduced elements per k-step
+        u32x4 raw[KS];
+        lds_read_sub(ring_addr + ((u / RG::SPS) % RG::NS) * RG::STAGE + (u % RG::SPS) * 32 * (2 * D),
+                     roff, raw);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+        float sc = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, raw[ks]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = ks * PER; e < (ks + 1) * PER; ++e)
+                sc = fmaf(wv[e >> 4][e & 15], relu_bits(prev[e >> 4][e & 15]), sc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return add_upper_half(sc);
+    };
     float* orow = a.out + y * a.out_stride;
     auto store = [&](int32_t u, float sc) {
         const int32_t slot = slot_begin + u * 32 + m;
@@ -680,24 +713,27 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
 #pragma unroll
     for (int s = 0; s < RG::NS - 1; ++s)
         if (s < n_st) fetch(s);
-    // sub-block u is the (u & 1) half of stage u / 2.  The MFMAs of u + 1 are
-    // issued before the VALU reduction of u (two accumulator sets), and the
-    // store of an even sub-block waits until after the next barrier so that
-    // the stage waits never cover a store just issued.
+    // Sub-block u is part u % SPS of stage u / SPS.  The MFMAs of u + 1 are
+    // issued together with the VALU reduction of u (two accumulator sets),
+    // and the store of an even sub-block waits until after a following
+    // barrier so that the stage waits never cover a store just issued.
     f32x16 acc0[MB], acc1[MB];
     sync(0);
     mfma_sub(0, acc0);
-    for (int32_t u = 0; u < nsub; u += 2) {
-        if (u + 1 < nsub) mfma_sub(u + 1, acc1);
-        const float s0 = reduce(acc0);
-        if (u + 2 < nsub) {
-            sync((u + 2) >> 1);
-            store(u, s0);
-            mfma_sub(u + 2, acc0);
-        } else {
-            store(u, s0);
-        }
-        if (u + 1 < nsub) store(u + 1, reduce(acc1));
+    int32_t u = 0;
+    for (; u + 2 < nsub; u += 2) {
+        const float s0 = mfma_reduce(u + 1, acc1, acc0);
+        if ((u + 2) % RG::SPS == 0) sync((u + 2) / RG::SPS);
+        store(u, s0);
+        const float s1 = mfma_reduce(u + 2, acc0, acc1);
+        store(u + 1, s1);
+    }
+    if (u + 1 < nsub) {
+        mfma_sub(u + 1, acc1);
+        store(u, reduce(acc0));
+        store(u + 1, reduce(acc1));
+    } else {
+        store(u, reduce(acc0));
     }
     wait_vmcnt<0>();
 }
@@ -708,7 +744,7 @@ hipError_t launch_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream)
     const int64_t n_seq = (a.rows.y0 + n_rows - 1) / R - a.rows.y0 / R + 1;
     const int64_t per_seq = (std::min<int64_t>(n_rows, R) + NW - 1) / NW;
     // segments: a multiple of the stage, sized for a few workgroups per CU
-    const int64_t want = n_rows * (int64_t)a.n_cols / (NW * 4096);
+    const int64_t want = n_rows * (int64_t)a.n_cols / (NW * 2048);
     int64_t seg = std::min<int64_t>(4096, std::max<int64_t>(512, (want + 63) / 64 * 64));
     while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
     dim3 grid((unsigned)(n_seq * per_seq), (unsigned)((a.n_cols + seg - 1) / seg));

@@ -30,7 +30,8 @@ struct VisRule {
 
     __host__ __device__ inline int32_t tokens(int32_t t) const {
         int64_t p = (int64_t)q_pos0 + t;
-        int64_t v = p >= 0 ? p / ratio : -((-p + ratio - 1) / ratio);  // floor division
+        // floor division (skipped for the common ratio 1)
+        int64_t v = ratio == 1 ? p : p >= 0 ? p / ratio : -((-p + ratio - 1) / ratio);
         if (v < 0) return 0;
         return v + 1 < n_k ? (int32_t)(v + 1) : n_k;
     }
