@@ -8,11 +8,12 @@
 // is the only one.  fp64 -> bf16 goes through a round-to-odd fp32
 // intermediate, which keeps that rounding single.
 //
-// The kernel streams the key cache once and is HBM-bound.  A workgroup of
-// 256 threads owns G = 256 / D consecutive blocks, one thread per (block,
-// dim).  Keys are staged through LDS in chunks of up to 64 rows: the
-// workgroup reads each block's chunk as one contiguous run with 16-byte
-// loads, then every thread walks its column of the chunk in key order.
+// The kernel streams the key cache once and is HBM-bound.  Each thread owns
+// one 16-byte column piece of one block (16 fp8 or 8 bf16 dimensions) and
+// walks the block's key rows in order, so every output keeps the sequential
+// sum; eight rows are loaded ahead (nontemporal 16-byte loads: every key
+// byte is read exactly once).  The threads of a wave cover one row of
+// several consecutive blocks, each as whole 128-byte lines.
 #include "tks_launch.hpp"
 
 namespace tks {
@@ -20,7 +21,7 @@ namespace tks {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;  // key rows staged per block and step
+constexpr int kAhead = 8;  // key rows loaded ahead per thread
 
 __device__ inline uint16_t f64_to_bf16_rne(double x) {
     // round-to-odd to fp32 (24 bits >= 8 + 2), then nearest-even to bf16
@@ -33,68 +34,72 @@ __device__ inline uint16_t f64_to_bf16_rne(double x) {
 
 template <bool FP8, int D>
 __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a, int64_t n_blocks) {
-    constexpr int G = kThreads / D;              // blocks per workgroup
-    constexpr int ROW = FP8 ? D : 2 * D;         // bytes per key row
-    constexpr int STRIDE = kChunk * ROW;         // LDS bytes per block
-    __shared__ __align__(16) uint8_t s_keys[G * STRIDE];
-    __shared__ float s_scale[FP8 ? G * kChunk : 1];
-
-    const int tid = threadIdx.x;
-    const int g = tid / D, d = tid % D;
+    constexpr int EPT = FP8 ? 16 : 8;   // key elements per 16-byte piece
+    constexpr int TPB = D / EPT;         // threads per block (pieces per row)
+    constexpr int ROW = FP8 ? D : 2 * D; // bytes per key row
+    const int64_t gt = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t bj = gt / TPB;         // pooled block over all sequences
+    const int part = (int)(gt % TPB);
+    if (bj >= n_blocks) return;
     const int64_t nb = a.n_k / a.block;
-    const int64_t bj0 = (int64_t)blockIdx.x * G;
-    const int64_t bj = bj0 + g;                  // this thread's block
-    const int ch = a.block < kChunk ? a.block : kChunk;
-    const int vec_per_block = ch * ROW / 16;
-    double acc = 0.0;
+    const int64_t row0 = (bj / nb) * a.n_k + (bj % nb) * a.block;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k) + row0 * ROW + part * 16;
+    const float* scl = FP8 ? a.k_scale + row0 : nullptr;
 
-    for (int c0 = 0; c0 < a.block; c0 += ch) {
-        // stage rows c0 .. c0+ch-1 of every block of the workgroup
-        for (int v = tid; v < G * vec_per_block; v += kThreads) {
-            const int gg = v / vec_per_block, off = (v % vec_per_block) * 16;
-            const int64_t b2 = bj0 + gg;
-            if (b2 < n_blocks) {
-                const int64_t row0 = (b2 / nb) * a.n_k + (b2 % nb) * a.block + c0;
-                // each block chunk is contiguous: whole lines, streamed once
-                const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                    reinterpret_cast<const uint8_t*>(a.k) + row0 * ROW + off));
-                *reinterpret_cast<u32x4*>(&s_keys[gg * STRIDE + off]) = x;
-            }
-        }
+    double acc[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
+    // the block size is a multiple of kAhead (32 .. 256)
+    for (int s0 = 0; s0 < a.block; s0 += kAhead) {
+        u32x4 v[kAhead];
+        float sc[kAhead];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i)
+            v[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(src + (int64_t)(s0 + i) * ROW));
         if (FP8) {
-            for (int v = tid; v < G * ch; v += kThreads) {
-                const int gg = v / ch, s = v % ch;
-                const int64_t b2 = bj0 + gg;
-                if (b2 < n_blocks)
-                    s_scale[gg * kChunk + s] =
-                        a.k_scale[(b2 / nb) * a.n_k + (b2 % nb) * a.block + c0 + s];
-            }
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) sc[i] = scl[s0 + i];
         }
-        __syncthreads();
-        if (bj < n_blocks) {
-            const uint8_t* col = &s_keys[g * STRIDE];
-#pragma unroll 8
-            for (int s = 0; s < ch; ++s) {
-                if (FP8) {
-                    const int code = col[s * ROW + d];
-                    const float v = __builtin_amdgcn_cvt_f32_fp8(code, 0);
-                    // scale * code is exact in fp64, so one fused rounding = add
-                    acc = fma((double)s_scale[g * kChunk + s], (double)v, acc);
-                } else {
-                    const uint32_t h = *reinterpret_cast<const uint16_t*>(col + s * ROW + 2 * d);
-                    acc += (double)__uint_as_float(h << 16);
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) {
+            if constexpr (FP8) {
+                // scale * code is exact in fp64, so the fma rounds once, like
+                // the sum of the exact products
+                const double sd = (double)sc[i];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i][w], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i][w], true);
+                    acc[4 * w + 0] = fma(sd, (double)lo[0], acc[4 * w + 0]);
+                    acc[4 * w + 1] = fma(sd, (double)lo[1], acc[4 * w + 1]);
+                    acc[4 * w + 2] = fma(sd, (double)hi[0], acc[4 * w + 2]);
+                    acc[4 * w + 3] = fma(sd, (double)hi[1], acc[4 * w + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    acc[2 * w + 0] += (double)__uint_as_float(v[i][w] << 16);
+                    acc[2 * w + 1] += (double)__uint_as_float(v[i][w] & 0xFFFF0000u);
                 }
             }
         }
-        __syncthreads();
     }
-    if (bj < n_blocks) a.out[bj * D + d] = f64_to_bf16_rne(acc / (double)a.block);
+    // EPT bf16 results = 16 (bf16) or 32 (fp8) contiguous bytes
+    uint32_t o[EPT / 2];
+#pragma unroll
+    for (int e = 0; e < EPT / 2; ++e)
+        o[e] = (uint32_t)f64_to_bf16_rne(acc[2 * e] / (double)a.block) |
+               ((uint32_t)f64_to_bf16_rne(acc[2 * e + 1] / (double)a.block) << 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(a.out + bj * D + part * EPT);
+#pragma unroll
+    for (int e = 0; e < EPT / 8; ++e) dst[e] = u32x4{o[4 * e], o[4 * e + 1], o[4 * e + 2], o[4 * e + 3]};
 }
 
 template <bool FP8, int D>
 void launch_d(const PoolArgs& a, int64_t n_blocks, hipStream_t stream) {
-    constexpr int G = kThreads / D;
-    const unsigned grid = (unsigned)((n_blocks + G - 1) / G);
+    constexpr int TPB = D / (FP8 ? 16 : 8);
+    const unsigned grid = (unsigned)((n_blocks * TPB + kThreads - 1) / kThreads);
     hipLaunchKernelGGL((pool_kernel<FP8, D>), dim3(grid), dim3(kThreads), 0, stream, a, n_blocks);
 }
 
