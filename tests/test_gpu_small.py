@@ -358,6 +358,50 @@ def test_topk_scores_matches_full_sort(n_cols, topk):
         np.testing.assert_array_equal(gv[r][ok], sc[r][want[ok]] + np.float32(0.0))
 
 
+def test_topk_scores_threshold_prefilter_cases():
+    """Rows longer than the LDS pool take a sampled threshold; every way the
+    sample can mislead (the best scores hidden between sample positions, a
+    tie block straddling the threshold, a pool that would overflow) must
+    still give the exact result.  Many rows use the narrow workgroups."""
+    say("topk_scores prefilter cases")
+    rng = np.random.default_rng(77)
+    for R, n_cols, topk in [(16, 70000, 2048), (600, 5000, 2048), (600, 20000, 300),
+                            (600, 17000, 2048)]:
+        sc = rng.standard_normal((R, n_cols)).astype(np.float32)
+        pos = (np.arange(2048) * n_cols) // 2048            # the sampled columns
+        hidden = np.setdiff1d(np.arange(n_cols), pos)[:topk]
+        sc[0] = 0.0
+        sc[0, hidden] = 1.0                                  # best keys never sampled
+        sc[1] = 0.0
+        sc[1, pos[: min(len(pos), topk // 4)]] = 2.0         # a few sampled, rest tied
+        sc[2] = rng.integers(0, 3, n_cols).astype(np.float32)  # three huge tie groups
+        top = rng.standard_normal(n_cols).astype(np.float32)
+        top[: topk // 2] = 50.0 + np.arange(topk // 2, dtype=np.float32)
+        top[topk // 2: topk // 2 + 6000 if n_cols > 7000 else n_cols] = 10.0   # tie block at the k-th
+        sc[3] = top
+        sc[4] = np.sort(rng.standard_normal(n_cols)).astype(np.float32)  # monotone row
+        idx, vals = tks.topk_scores(dev(sc), topk)
+        torch.cuda.synchronize()
+        gi, gv = host(idx), host(vals)
+        full = np.full(R, n_cols, np.int32)
+        for r in range(R):
+            want = brute(sc[r], full[r], topk)
+            np.testing.assert_array_equal(gi[r], want, err_msg="R=%d n=%d row %d" % (R, n_cols, r))
+            ok = want >= 0
+            np.testing.assert_array_equal(gv[r][ok], sc[r][want[ok]] + np.float32(0.0))
+
+
+def test_tiled_rows_with_prior_list_take_the_prefilter_exactly():
+    """Key tiles longer than the LDS pool plus the running list of earlier
+    tiles: the sampled threshold covers both, integer scores (many ties)."""
+    say("tiled prefilter with running list")
+    sh, x = int_case(63, n_q=600, n_k=36000, heads=4, dim=32, q_pos0=35400, lo=-3, hi=3)
+    oi, ov = oracle_flat(sh, x, 2048)
+    for qc, kt in [(600, 16384), (256, 20000), (600, 4096)]:
+        gi, gv = gpu_flat(sh, x, 2048, qc, kt)
+        assert_topk_exact(gi, gv, oi, ov, "tiled prefilter qc=%d kt=%d" % (qc, kt))
+
+
 # ------------------------------------------------------------------- HISA
 
 def test_hisa_all_blocks_kept_equals_flat():

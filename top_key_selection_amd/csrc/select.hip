@@ -39,6 +39,8 @@ constexpr int kMaxK = 2048;
 constexpr int kCap = 4096;          // LDS candidate list (entries of the threshold bin)
 constexpr int kBins = 4096;         // 12-bit first digit
 constexpr int kBinShift = 20;
+constexpr int kSamples = 2048;      // candidates sampled for the prefilter threshold
+constexpr int kPrefilterMin = 16384; // rows at least this long take the prefilter
 constexpr int kMaxBlkEntries = 512;
 
 // LDS of the selection kernels: selected list [0, kMaxK), candidate list
@@ -46,6 +48,7 @@ constexpr int kMaxBlkEntries = 512;
 // list; the radix fallback uses the selected list and 4 KiB after it.
 struct SelectLds {
     uint64_t u[kMaxK + kCap];
+    uint32_t hist8[256];  // digit histogram of the candidate resolution
     int32_t blk[kMaxBlkEntries];
     int32_t wsum[kMaxWaves];
     int32_t pick[8];
@@ -218,30 +221,158 @@ __device__ __forceinline__ void find_threshold(G&& get, int32_t K, int32_t* pick
     __syncthreads();
 }
 
-// Sort u[0, n) descending (bitonic over the next power of two, zero padded,
-// at most cap entries).
-template <int NT>
-__device__ __forceinline__ void sort_desc(uint64_t* u, int32_t n, int32_t cap) {
-    const int tid = threadIdx.x;
-    int32_t P2 = 1;
-    while (P2 < n) P2 <<= 1;
-    if (P2 > cap) P2 = cap;
-    for (int i = n + tid; i < P2; i += NT) u[i] = 0;
-    __syncthreads();
-    for (int size = 2; size <= P2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (P2 >> 1); i += NT) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t x = u[lo], z = u[hi];
-                if ((x < z) == desc) {
-                    u[lo] = z;
-                    u[hi] = x;
-                }
+// Value of lane ^ S, exchanged by the vector ALU (DPP quad permutes and row
+// shifts, v_permlane16/32_swap) rather than through the LDS crossbar.
+template <int S>
+__device__ __forceinline__ uint32_t xchg32(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (S == 1) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (S == 2) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (S == 4 || S == 8) {
+        // row_shl:S reads lane + S, row_shr:S reads lane - S
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x100 + S, 0xF, 0xF, false);
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x110 + S, 0xF, 0xF, false);
+        return (lane & S) ? dn : up;
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(S == 32, "exchange stride");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t xchg64(uint64_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return ((uint64_t)xchg32<S>((uint32_t)(v >> 32)) << 32) | xchg32<S>((uint32_t)v);
+#else
+    return v;  // the permlane builtins exist for the device pass only
+#endif
+}
+
+// One compare-exchange stage at lane stride S (< 64) of a bitonic network
+// over 128 entries (entry `lane` in a[c], `lane + 64` in b[c]).
+template <int S, int N>
+__device__ __forceinline__ void cx_lanes(uint64_t* a, uint64_t* b, int size) {
+    const int lane = threadIdx.x & 63;
+    const bool lower = (lane & S) == 0;  // same for lane + 64
+    const bool keep_a = ((lane & size) == 0) == lower;
+    const bool keep_b = (((lane + 64) & size) == 0) == lower;
+    uint64_t pa[N], pb[N];
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        pa[c] = xchg64<S>(a[c]);
+        pb[c] = xchg64<S>(b[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        a[c] = keep_a ? (a[c] > pa[c] ? a[c] : pa[c]) : (a[c] < pa[c] ? a[c] : pa[c]);
+        b[c] = keep_b ? (b[c] > pb[c] ? b[c] : pb[c]) : (b[c] < pb[c] ? b[c] : pb[c]);
+    }
+}
+
+// Bitonic sort of N independent 128-entry chunks held by one wave, each
+// descending; the chunks go through the network together.
+template <int N>
+__device__ __forceinline__ void wave_sort128(uint64_t* a, uint64_t* b) {
+#pragma unroll
+    for (int size = 2; size <= 128; size <<= 1) {
+        if (size == 128) {
+            // one descending block: a holds the lower index of each pair
+#pragma unroll
+            for (int c = 0; c < N; ++c) {
+                const uint64_t hi = a[c] > b[c] ? a[c] : b[c];
+                const uint64_t lo = a[c] > b[c] ? b[c] : a[c];
+                a[c] = hi;
+                b[c] = lo;
             }
-            __syncthreads();
         }
+        if (size >= 64) cx_lanes<32, N>(a, b, size);
+        if (size >= 32) cx_lanes<16, N>(a, b, size);
+        if (size >= 16) cx_lanes<8, N>(a, b, size);
+        if (size >= 8) cx_lanes<4, N>(a, b, size);
+        if (size >= 4) cx_lanes<2, N>(a, b, size);
+        cx_lanes<1, N>(a, b, size);
+    }
+}
+
+// Sort u[0, n) descending, n <= kMaxK; the entries must be distinct (the
+// composites are).  tmp has room for the padded size.  Waves sort 128-entry
+// chunks in registers; the chunks are then merged pairwise, each entry
+// finding its place in the partner run by binary search (its rank in the
+// merged run is its own position plus the partner entries above it).  A
+// thread's searches advance in lockstep so their LDS reads overlap.
+template <int NT>
+__device__ __forceinline__ void sort_desc(uint64_t* u, uint64_t* tmp, int32_t n) {
+    constexpr int W = NT / kWave;
+    constexpr int CPW = (kMaxK / 128 + W - 1) / W;  // chunks per wave
+    constexpr int EPT = (kMaxK + NT - 1) / NT;      // merge entries per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (n <= 1) return;
+    int32_t P = 128;
+    while (P < n) P <<= 1;
+    // padding: distinct values below every real composite
+    for (int i = n + tid; i < P; i += NT) u[i] = (uint64_t)(P - i);
+    __syncthreads();
+    {
+        const int n_chunks = P / 128;
+        uint64_t a[CPW], b[CPW];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int ch = wave + c * W;
+            a[c] = ch < n_chunks ? u[ch * 128 + lane] : 0;
+            b[c] = ch < n_chunks ? u[ch * 128 + 64 + lane] : 0;
+        }
+        wave_sort128<CPW>(a, b);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int ch = wave + c * W;
+            if (ch < n_chunks) {
+                u[ch * 128 + lane] = a[c];
+                u[ch * 128 + 64 + lane] = b[c];
+            }
+        }
+    }
+    __syncthreads();
+    uint64_t* src = u;
+    uint64_t* dst = tmp;
+    for (int32_t L = 128; L < P; L <<= 1) {
+        uint64_t x[EPT];
+        int32_t k[EPT], other[EPT], at[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = tid + e * NT;
+            const int32_t run = i / L;
+            const int32_t base = (run & ~1) * L;
+            x[e] = i < P ? src[i] : 0;
+            other[e] = base + ((run & 1) ? 0 : L);
+            at[e] = base + (i & (L - 1));
+            k[e] = 0;
+        }
+        for (int32_t step = L >> 1; step > 0; step >>= 1) {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (tid + e * NT < P && src[other[e] + k[e] + step - 1] > x[e]) k[e] += step;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            if (tid + e * NT < P) {
+                if (src[other[e] + k[e]] > x[e]) ++k[e];
+                dst[at[e] + k[e]] = x[e];
+            }
+        }
+        __syncthreads();
+        uint64_t* t = src;
+        src = dst;
+        dst = t;
+    }
+    if (src != u) {
+        for (int i = tid; i < n; i += NT) u[i] = src[i];
+        __syncthreads();
     }
 }
 
@@ -258,7 +389,7 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, const RowCtx& r, 
             sel[i] = ((uint64_t)(uint32_t)c << 32) | (c >> 32);
         }
         __syncthreads();
-        sort_desc<NT>(sel, n_sel, kMaxK);
+        sort_desc<NT>(sel, &L.u[kMaxK], n_sel);
         const int32_t Lb = r.n_tok > 0 ? (r.n_tok - 1) / a.sel_block : -1;
         const bool f_first = (a.force_flags & 1u) && Lb > 0;
         const bool f_local = (a.force_flags & 2u) && Lb >= 0;
@@ -436,19 +567,92 @@ __device__ __forceinline__ int32_t radix_fallback(const SelectArgs& a, const Row
     return n_gt + need;
 }
 
-// Finish after pass 2: sel[0, n_gt) filled; cand[0, n_cand) holds the
-// threshold bin; take its best `need`.  Returns the selected count.
+// sel[0, n_gt) is filled; cand[0, n_cand) holds composites that agree on
+// every bit above bit first_shift + 8.  The best `need` candidates are
+// appended to sel by an exact radix select, 8-bit digits from bit
+// first_shift down, entirely in LDS: each round histograms the digit of the
+// candidates that match every digit fixed so far, appends those above the
+// digit that holds the need-th best, and fixes that digit.  Returns the
+// selected count.
+//
+// `fixed` / `prefix` name bits already decided (a candidate is live while it
+// matches them) and `live` counts the live candidates.
 template <int NT>
 __device__ __forceinline__ int32_t finish_from_candidates(SelectLds& L, int32_t n_gt, int32_t n_cand,
-                                                 int32_t need) {
-    const int tid = threadIdx.x;
-    uint64_t* cand = &L.u[kMaxK];
-    if (need > 0) {
-        sort_desc<NT>(cand, n_cand, kCap);
-        for (int i = tid; i < need; i += NT) L.u[n_gt + i] = cand[i];
+                                                 int32_t need, int first_shift, uint64_t prefix = 0,
+                                                 uint64_t fixed = 0, int32_t live = -1) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t* cand = &L.u[kMaxK];
+    uint32_t* hist = L.hist8;
+    if (tid == 0) L.cnt[0] = n_gt;
+    __syncthreads();
+    const uint64_t all_bits = fixed | (first_shift >= 56 ? ~0ull : (1ull << (first_shift + 8)) - 1);
+    if (live < 0) live = n_cand;
+    for (int shift = first_shift; need > 0; shift = shift >= 8 ? shift - 8 : 0) {
+        auto is_live = [&](uint64_t e) { return ((e ^ prefix) & fixed) == 0; };
+        if (live <= need || fixed == all_bits) {
+            // every remaining candidate is selected
+            for (int base = 0; base < n_cand; base += NT) {
+                const int i = base + tid;
+                const uint64_t e = i < n_cand ? cand[i] : 0;
+                const bool p = i < n_cand && is_live(e);
+                const int32_t pos = wave_append(&L.cnt[0], p);
+                if (p) L.u[pos] = e;
+            }
+            break;
+        }
+        for (int i = tid; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n_cand; i += NT) {
+            const uint64_t e = cand[i];
+            if (is_live(e)) atomicAdd(&hist[(uint32_t)(e >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int32_t c[4], lsum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[i] = (int32_t)hist[255 - (4 * lane + i)];
+                lsum += c[i];
+            }
+            int32_t inc = lsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int32_t v = __shfl_up(inc, o);
+                if (lane >= o) inc += v;
+            }
+            const int32_t excl = inc - lsum;
+            if (excl < need && need <= inc) {
+                int32_t cum = excl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (cum < need && need <= cum + c[i]) {
+                        L.pick[0] = 255 - (4 * lane + i);
+                        L.pick[1] = cum;
+                        L.pick[2] = c[i];
+                    }
+                    cum += c[i];
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t d = (uint32_t)L.pick[0];
+        const int32_t above = L.pick[1], in = L.pick[2];
+        for (int base = 0; base < n_cand; base += NT) {
+            const int i = base + tid;
+            const uint64_t e = i < n_cand ? cand[i] : 0;
+            const bool p = i < n_cand && is_live(e) && ((uint32_t)(e >> shift) & 255u) > d;
+            const int32_t pos = wave_append(&L.cnt[0], p);
+            if (p) L.u[pos] = e;
+        }
+        need -= above;
+        live = in;
+        prefix |= (uint64_t)d << shift;
+        fixed |= 255ull << shift;
+        __syncthreads();
     }
     __syncthreads();
-    return n_gt + need;
+    return L.cnt[0];
 }
 
 template <int NT>
@@ -477,10 +681,10 @@ __device__ __forceinline__ void setup_row(const SelectArgs& a, RowCtx& r, Select
 
 // ------------------------------------------------- one workgroup per row
 
-// Exact selection of the row's top-K candidates into L.u[0, n) (unsorted);
-// returns n.
+// Exact selection by a full histogram of the row (the path that never
+// fails): the row's top-K candidates into L.u[0, n) (unsorted); returns n.
 template <bool VEC, int NT>
-__device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
+__device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
     const int tid = threadIdx.x;
     if (K <= 0) return 0;
     uint32_t* hist = lds_hist(L);
@@ -519,7 +723,145 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
     __syncthreads();
     if (all) return total;
     if (whole_bin) return K;
-    return finish_from_candidates<NT>(L, above, inbin, K - above);
+    return finish_from_candidates<NT>(L, above, inbin, K - above, 44);
+}
+
+// Key threshold that about `target` of the row's n candidates (prior list,
+// then columns) reach, estimated from kSamples evenly spaced candidates:
+// the key of the sample of rank target * valid_samples / n, resolved to 20
+// bits with two 12-bit LDS histograms.  n > kSamples.  Returns false when
+// the sample cannot place it.
+template <int NT>
+__device__ __forceinline__ bool sample_threshold(const SelectArgs& a, const RowCtx& r, SelectLds& L,
+                                                 int32_t n, int32_t target, uint32_t& tau) {
+    const int tid = threadIdx.x;
+    const int32_t np = r.prior ? prior_len(a) : 0;
+    uint32_t* keys = reinterpret_cast<uint32_t*>(&L.u[kMaxK]);  // kSamples keys (0: no candidate)
+    uint32_t* hist = reinterpret_cast<uint32_t*>(L.u);          // kBins bins
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    if (tid == 0) L.cnt[0] = 0;
+    __syncthreads();
+    for (int s = tid; s < kSamples; s += NT) {
+        const int32_t q = (int32_t)(((int64_t)s * n) / kSamples);
+        bool v;
+        float x;
+        if (q < np) {
+            v = a.prior_idx[r.y * np + q] >= 0;
+            x = a.prior_val[r.y * np + q];
+        } else {
+            const int32_t j = r.lo + (q - np);
+            v = column_index(a, r, j) >= 0;
+            x = r.srow[j];
+        }
+        const uint32_t key = v ? score_key(x) : 0u;
+        keys[s] = key;
+        hist_add(hist, v, key >> kBinShift);
+        const uint64_t m = __ballot(v);
+        if ((threadIdx.x & 63) == 0 && m) atomicAdd(&L.cnt[0], (int32_t)__popcll(m));
+    }
+    __syncthreads();
+    const int32_t sv = L.cnt[0];
+    const int64_t rs = ((int64_t)target * sv + n - 1) / n;
+    if (rs < 1 || rs >= sv) return false;
+    find_threshold<NT>([&](int b) { return hist[b]; }, (int32_t)rs, L.pick, L.wsum);
+    const int32_t b1 = L.pick[0];
+    const int32_t r2 = (int32_t)rs - L.pick[1];
+    __syncthreads();
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int s = tid; s < kSamples; s += NT) {
+        const uint32_t k = keys[s];
+        hist_add(hist, k != 0u && (int32_t)(k >> kBinShift) == b1, (k >> 8) & (kBins - 1));
+    }
+    __syncthreads();
+    find_threshold<NT>([&](int b) { return hist[b]; }, r2, L.pick, L.wsum);
+    const int32_t b2 = L.pick[0];
+    tau = ((uint32_t)b1 << kBinShift) | (b2 >= 0 ? (uint32_t)b2 << 8 : 0u);
+    __syncthreads();
+    return true;
+}
+
+// Exact selection of the row's top-K candidates into L.u[0, n) (unsorted);
+// returns n.
+//
+// Threshold prefilter (the threshold-based Indexer-TopK abstract listed on
+// the StreamIndex page: bin the scores and keep only candidates above a
+// tight threshold, the result staying exact): a row with more candidates
+// than the LDS pool holds gets a key threshold from a sample, sized for
+// about 1.4 K candidates; one pass keeps every candidate at or above it
+// in the LDS pool.  If the pool holds at least K candidates, every
+// candidate left out ranks below all of them, so the pool's best K are the
+// answer; they are found by an LDS radix select.  A pool that is too small
+// or overflows falls back to the full histogram path.
+template <bool VEC, int NT>
+__device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
+    const int tid = threadIdx.x;
+    if (K <= 0) return 0;
+    const int32_t n_cols = max(0, r.hi - r.lo);
+    const int32_t n_total = n_cols + (r.prior ? prior_len(a) : 0);
+    uint64_t* cand = &L.u[kMaxK];
+    uint32_t tau = 0;
+    if (n_total > K && n_total < kPrefilterMin) return select_hist<VEC, NT>(a, r, L, K);
+    if (n_total > kCap) {
+        const int32_t target = K + K / 2 - K / 10 + 32;
+        if (!sample_threshold<NT>(a, r, L, n_total, target, tau)) return select_hist<VEC, NT>(a, r, L, K);
+    }
+    // one pass: the pool of candidates with key >= tau (all of them when
+    // tau = 0); a row that fits the answer goes straight to the list
+    const bool direct = n_total <= K;
+    uint64_t* dst = direct ? L.u : cand;
+    const int32_t cap = direct ? kMaxK : kCap;
+    if (tid == 0) L.cnt[1] = 0;
+    __syncthreads();
+    auto c = [&](bool valid, uint32_t key, int32_t idx) {
+        const bool p = valid && key >= tau;
+        const int32_t pos = wave_append(&L.cnt[1], p);
+        if (p && pos < cap) dst[pos] = composite(key, idx);
+    };
+    visit_prior<NT>(a, r, c);
+    visit_columns<VEC, NT>(a, r, r.lo, r.hi, c);
+    __syncthreads();
+    const int32_t n_pool = L.cnt[1];
+    if (direct) return n_pool;
+    if (tau == 0u && n_pool <= K) {
+        // fewer valid candidates than K (block slots without a key)
+        for (int i = tid; i < n_pool; i += NT) L.u[i] = cand[i];
+        __syncthreads();
+        return n_pool;
+    }
+    if (n_pool < K || n_pool > kCap) {
+        __syncthreads();
+        return select_hist<VEC, NT>(a, r, L, K);
+    }
+    if (n_pool == K) {
+        for (int i = tid; i < n_pool; i += NT) L.u[i] = cand[i];
+        __syncthreads();
+        return K;
+    }
+    // first digit: the top 12 bits, histogrammed in the still empty list
+    uint32_t* hist = reinterpret_cast<uint32_t*>(L.u);
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_pool; base += NT) {
+        const int i = base + tid;
+        hist_add(hist, i < n_pool, i < n_pool ? (uint32_t)(cand[i] >> 52) : 0u);
+    }
+    __syncthreads();
+    find_threshold<NT>([&](int b) { return hist[b]; }, K, L.pick, L.wsum);
+    const int32_t b = L.pick[0], above = L.pick[1], inbin = L.pick[2];
+    __syncthreads();
+    if (tid == 0) L.cnt[0] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_pool; base += NT) {
+        const int i = base + tid;
+        const uint64_t e = i < n_pool ? cand[i] : 0;
+        const bool p = i < n_pool && (int32_t)(e >> 52) > b;
+        const int32_t pos = wave_append(&L.cnt[0], p);
+        if (p) L.u[pos] = e;
+    }
+    __syncthreads();
+    return finish_from_candidates<NT>(L, above, n_pool, K - above, 44, (uint64_t)b << 52,
+                                      0xFFFull << 52, inbin);
 }
 
 template <bool VEC, int NT>
@@ -543,7 +885,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
         r.hi = max(c0, c1);
         const int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
         __syncthreads();
-        sort_desc<NT>(L.u, n_sel, kMaxK);
+        sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
         const int64_t o = r.y * (int64_t)a.run_stride + (int64_t)p * K;
         for (int j = tid; j < K; j += NT) {
             int32_t id = -1;
@@ -565,7 +907,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     if (a.parts > 0) r.hi = r.lo;
     int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
     __syncthreads();
-    sort_desc<NT>(L.u, n_sel, kMaxK);
+    sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
     if (a.parts > 0) {
         // exact iff every truncated partition's last kept candidate ranks
         // no higher than the merged k-th (dropped candidates rank below it)
@@ -588,7 +930,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
             __syncthreads();
             n_sel = select_core<VEC, NT>(a, r, L, K);
             __syncthreads();
-            sort_desc<NT>(L.u, n_sel, kMaxK);
+            sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
         }
     }
     write_row<NT>(a, r, L, n_sel, final_out);
