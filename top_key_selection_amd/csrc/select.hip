@@ -268,10 +268,13 @@ __device__ __forceinline__ void cx_lanes(uint64_t* a, uint64_t* b, int size) {
         pa[c] = xchg64<S>(a[c]);
         pb[c] = xchg64<S>(b[c]);
     }
+    // entries are distinct: take the partner's value when it is the larger
+    // one and this position keeps the larger, or the smaller and keeps the
+    // smaller
 #pragma unroll
     for (int c = 0; c < N; ++c) {
-        a[c] = keep_a ? (a[c] > pa[c] ? a[c] : pa[c]) : (a[c] < pa[c] ? a[c] : pa[c]);
-        b[c] = keep_b ? (b[c] > pb[c] ? b[c] : pb[c]) : (b[c] < pb[c] ? b[c] : pb[c]);
+        a[c] = ((pa[c] > a[c]) == keep_a) ? pa[c] : a[c];
+        b[c] = ((pb[c] > b[c]) == keep_b) ? pb[c] : b[c];
     }
 }
 
@@ -907,7 +910,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     if (a.parts > 0) r.hi = r.lo;
     int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
     __syncthreads();
-    sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
+    // (block-select output is ordered by block index: write_row sorts it)
+    if (!a.blockselect) sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
     if (a.parts > 0) {
         // exact iff every truncated partition's last kept candidate ranks
         // no higher than the merged k-th (dropped candidates rank below it)
