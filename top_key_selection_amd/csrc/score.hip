@@ -48,6 +48,9 @@ __device__ inline void load_key(KeyFrag<D, FP8>& f, const void* k, int64_t row, 
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Block-list entries of one row (HISA kept blocks, forced ones included).
+constexpr int kMaxBlkEntries = 512;
+
 // max(0, x) in one integer max on the bit pattern: negative floats (and -0)
 // are negative integers, non-negative floats keep their order.  Inputs are
 // finite, so no NaN handling is needed.
@@ -138,14 +141,22 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
         }
 
     const int64_t kseq = (int64_t)seq * a.k_seq_len;
-    const int32_t* blk_row = BLOCKS ? a.blk + (a.rows.y0 + y) * a.blk_stride : nullptr;
     const int32_t bmask = (1 << a.block_shift) - 1;
+    // the row's block list, staged in LDS: a key address then never waits on
+    // a global load that the key loads already in flight would hold up
+    __shared__ int32_t s_blk[BLOCKS ? kMaxBlkEntries : 1];
+    if constexpr (BLOCKS) {
+        const int32_t* blk_row = a.blk + (a.rows.y0 + y) * a.blk_stride;
+        const int32_t n_ent = (a.n_cols + bmask) >> a.block_shift;
+        for (int i = threadIdx.x; i < n_ent; i += 256) s_blk[i] = blk_row[i];
+        __syncthreads();
+    }
 
     auto key_of = [&](int32_t slot, bool& valid) -> int32_t {
         int32_t key;
         if (BLOCKS) {
             // the block list is only read for slots inside the row
-            const int32_t b = slot < limit ? blk_row[slot >> a.block_shift] : -1;
+            const int32_t b = slot < limit ? s_blk[slot >> a.block_shift] : -1;
             // blocks past the last visible key are skipped before the shift
             const bool ok = b >= 0 && b <= ((n_tok - 1) >> a.block_shift);
             key = ok ? (b << a.block_shift) + (slot & bmask) : 0;
@@ -322,11 +333,19 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     bf16x8 qa[MB][KS];  // loaded after the first ring copies are issued
     float wv[MB][16];
     const int64_t kseq = (int64_t)seq * a.k_seq_len;
-    const int32_t* blk_row = BLOCKS ? a.blk + (a.rows.y0 + y) * a.blk_stride : nullptr;
     const int32_t bmask = (1 << a.block_shift) - 1;
+    // the row's block list in LDS (see score_kernel); staged before the first
+    // key copies, which need it for their addresses
+    __shared__ int32_t s_blk[BLOCKS ? kMaxBlkEntries : 1];
+    if constexpr (BLOCKS) {
+        const int32_t* blk_row = a.blk + (a.rows.y0 + y) * a.blk_stride;
+        const int32_t n_ent = (a.n_cols + bmask) >> a.block_shift;
+        for (int i = threadIdx.x; i < n_ent; i += 256) s_blk[i] = blk_row[i];
+        __syncthreads();
+    }
     auto key_of = [&](int32_t slot, bool& valid) -> int32_t {
         if (BLOCKS) {
-            const int32_t b = slot < limit ? blk_row[slot >> a.block_shift] : -1;
+            const int32_t b = slot < limit ? s_blk[slot >> a.block_shift] : -1;
             const bool ok = b >= 0 && b <= ((n_tok - 1) >> a.block_shift);
             const int32_t key = ok ? (b << a.block_shift) + (slot & bmask) : 0;
             valid = ok && key < n_tok;
