@@ -42,6 +42,7 @@ constexpr int kBinShift = 20;
 constexpr int kSamples = 2048;      // candidates sampled for the prefilter threshold
 constexpr int kPrefilterMin = 16384; // rows at least this long take the prefilter
 constexpr int kMaxBlkEntries = 512;
+constexpr int kBitmapWords = 4096;  // block-select bitmap (ids below 131072)
 
 // LDS of the selection kernels: selected list [0, kMaxK), candidate list
 // [kMaxK, kMaxK + kCap).  The histogram of pass 1 aliases the candidate
@@ -386,13 +387,10 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, const RowCtx& r, 
     const int tid = threadIdx.x;
     uint64_t* sel = L.u;
     if (a.blockselect) {
-        // ascending block index: re-key with the index on top and sort again
-        for (int i = tid; i < n_sel; i += NT) {
-            const uint64_t c = sel[i];
-            sel[i] = ((uint64_t)(uint32_t)c << 32) | (c >> 32);
-        }
-        __syncthreads();
-        sort_desc<NT>(sel, &L.u[kMaxK], n_sel);
+        // ascending block index.  The selected block ids are distinct and
+        // small: mark them in an LDS bitmap, and each one's output slot is
+        // the number of marked ids below it (word prefix sums + popcount),
+        // so no sort is needed.  Very long block lists use a sort instead.
         const int32_t Lb = r.n_tok > 0 ? (r.n_tok - 1) / a.sel_block : -1;
         const bool f_first = (a.force_flags & 1u) && Lb > 0;
         const bool f_local = (a.force_flags & 2u) && Lb >= 0;
@@ -400,16 +398,71 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, const RowCtx& r, 
         int32_t* oi = a.out_idx + g * a.out_width;
         float* ov = a.out_val ? a.out_val + g * a.out_width : nullptr;
         const int32_t off = f_first ? 1 : 0;
+        const int32_t n_words = (a.col_key0 + a.n_cols + 31) / 32;
+        auto id_of = [](uint64_t c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); };
+        if (n_words <= kBitmapWords) {
+            uint32_t* bits = reinterpret_cast<uint32_t*>(&L.u[kMaxK]);
+            uint32_t* pre = bits + kBitmapWords;
+            for (int i = tid; i < n_words; i += NT) bits[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < n_sel; i += NT) {
+                const int32_t id = id_of(sel[i]);
+                atomicOr(&bits[id >> 5], 1u << (id & 31));
+            }
+            __syncthreads();
+            // exclusive prefix of the word popcounts, per thread a run of words
+            const int per = (n_words + NT - 1) / NT;
+            const int w0 = tid * per;
+            int32_t local = 0;
+            for (int i = 0; i < per; ++i)
+                if (w0 + i < n_words) local += __popc(bits[w0 + i]);
+            const int lane = tid & 63, wave = tid >> 6;
+            int32_t inc = local;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int32_t v = __shfl_up(inc, o);
+                if (lane >= o) inc += v;
+            }
+            if (lane == 63) L.wsum[wave] = inc;
+            __syncthreads();
+            int32_t run = inc - local;
+            for (int w = 0; w < wave; ++w) run += L.wsum[w];
+            for (int i = 0; i < per; ++i) {
+                if (w0 + i < n_words) {
+                    pre[w0 + i] = run;
+                    run += __popc(bits[w0 + i]);
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < n_sel; i += NT) {
+                const uint64_t c = sel[i];
+                const int32_t id = id_of(c);
+                const int32_t pos = pre[id >> 5] + __popc(bits[id >> 5] & ((1u << (id & 31)) - 1u));
+                oi[off + pos] = id;
+                if (ov) ov[off + pos] = key_score((uint32_t)(c >> 32));
+            }
+        } else {
+            // re-key with the index on top and sort
+            for (int i = tid; i < n_sel; i += NT) {
+                const uint64_t c = sel[i];
+                sel[i] = ((uint64_t)(uint32_t)c << 32) | (c >> 32);
+            }
+            __syncthreads();
+            sort_desc<NT>(sel, &L.u[kMaxK], n_sel);
+            for (int j = tid; j < n_sel; j += NT) {
+                const uint64_t c = sel[j];
+                oi[off + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)(c >> 32));
+                if (ov) ov[off + j] = key_score((uint32_t)c);
+            }
+        }
+        // forced blocks and padding around the selected run
         for (int j = tid; j < a.out_width; j += NT) {
+            if (j >= off && j < off + n_sel) continue;
             int32_t id = -1;
             float v = __builtin_nanf("");
             if (f_first && j == 0) {
                 id = 0;
                 v = __builtin_inff();
-            } else if (j - off < n_sel) {
-                const uint64_t c = sel[j - off];
-                id = (int32_t)(0xFFFFFFFFu - (uint32_t)(c >> 32));
-                v = key_score((uint32_t)c);
             } else if (f_local && j == off + n_sel) {
                 id = Lb;
                 v = __builtin_inff();
