@@ -11,8 +11,8 @@
 // The kernel streams the key cache once and is HBM-bound.  Each thread owns
 // one 16-byte column piece of one block (16 fp8 or 8 bf16 dimensions) and
 // walks the block's key rows in order, so every output keeps the sequential
-// sum; eight rows are loaded ahead (nontemporal 16-byte loads: every key
-// byte is read exactly once).  The threads of a wave cover one row of
+// sum; two batches of four rows are in flight, one summed while the next
+// loads (nontemporal 16-byte loads: every key byte is read exactly once).  The threads of a wave cover one row of
 // several consecutive blocks, each as whole 128-byte lines.
 #include "tks_launch.hpp"
 
@@ -20,8 +20,8 @@ namespace tks {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kAhead = 8;  // key rows loaded ahead per thread
+constexpr int kThreads = 64;  // one wave per workgroup: many small workgroups spread best
+constexpr int kAhead = 4;  // key rows per batch (two batches in flight)
 
 __device__ inline uint16_t f64_to_bf16_rne(double x) {
     // round-to-odd to fp32 (24 bits >= 8 + 2), then nearest-even to bf16
@@ -49,10 +49,10 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a, int64_t n_bl
     double acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
-    // the block size is a multiple of kAhead (32 .. 256)
-    for (int s0 = 0; s0 < a.block; s0 += kAhead) {
-        u32x4 v[kAhead];
-        float sc[kAhead];
+    // two batches of kAhead rows: one is summed while the next is in flight
+    u32x4 va[kAhead], vb[kAhead];
+    float sa[kAhead], sb[kAhead];
+    auto load = [&](u32x4* v, float* sc, int s0) {
 #pragma unroll
         for (int i = 0; i < kAhead; ++i)
             v[i] = __builtin_nontemporal_load(
@@ -61,6 +61,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a, int64_t n_bl
 #pragma unroll
             for (int i = 0; i < kAhead; ++i) sc[i] = scl[s0 + i];
         }
+    };
+    auto add = [&](const u32x4* v, const float* sc) {
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) {
             if constexpr (FP8) {
@@ -84,6 +86,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a, int64_t n_bl
                 }
             }
         }
+    };
+    // the block size is a multiple of 2 * kAhead (32 .. 256)
+    load(va, sa, 0);
+    for (int s0 = 0; s0 < a.block; s0 += 2 * kAhead) {
+        load(vb, sb, s0 + kAhead);
+        add(va, sa);
+        if (s0 + 2 * kAhead < a.block) load(va, sa, s0 + 2 * kAhead);
+        add(vb, sb);
     }
     // EPT bf16 results = 16 (bf16) or 32 (fp8) contiguous bytes
     uint32_t o[EPT / 2];
