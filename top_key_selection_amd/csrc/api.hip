@@ -171,7 +171,7 @@ FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_
     if (tiled) off += round_up(qc * (int64_t)topk * 4, 256);
     p.off_run_idx = off;
     if (tiled) off += round_up(qc * (int64_t)topk * 4, 256);
-    p.split = tiled ? tks::SelectSplit{0, 0, 0}
+    p.split = tiled ? tks::SelectSplit{0, 0}
                     : tks::select_split(qc, (int32_t)std::min<int64_t>(kt, maxvis), topk);
     p.off_split = off;
     off += tks::select_split_workspace(qc, p.split);

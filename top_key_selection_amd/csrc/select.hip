@@ -127,7 +127,7 @@ __device__ __forceinline__ void visit_columns(const SelectArgs& a, const RowCtx&
 }
 
 // Visit the prior list (running top-k of earlier key tiles).
-__device__ __forceinline__ int32_t prior_len(const SelectArgs& a) { return a.prior_len > 0 ? a.prior_len : a.topk; }
+__device__ __forceinline__ int32_t prior_len(const SelectArgs& a) { return a.topk; }
 
 template <int NT, class F>
 __device__ __forceinline__ void visit_prior(const SelectArgs& a, const RowCtx& r, F&& f) {
@@ -837,6 +837,43 @@ __device__ __forceinline__ bool sample_threshold(const SelectArgs& a, const RowC
     return true;
 }
 
+// The best K of the pool cand[0, n) (K <= n <= kCap) into L.u[0, K), exact:
+// a 12-bit first digit (histogram in the still empty list), then the LDS
+// radix select of finish_from_candidates.  Returns K.
+template <int NT>
+__device__ __forceinline__ int32_t resolve_pool(SelectLds& L, int32_t n_pool, int32_t K) {
+    const int tid = threadIdx.x;
+    const uint64_t* cand = &L.u[kMaxK];
+    if (n_pool == K) {
+        for (int i = tid; i < n_pool; i += NT) L.u[i] = cand[i];
+        __syncthreads();
+        return K;
+    }
+    uint32_t* hist = reinterpret_cast<uint32_t*>(L.u);
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_pool; base += NT) {
+        const int i = base + tid;
+        hist_add(hist, i < n_pool, i < n_pool ? (uint32_t)(cand[i] >> 52) : 0u);
+    }
+    __syncthreads();
+    find_threshold<NT>([&](int b) { return hist[b]; }, K, L.pick, L.wsum);
+    const int32_t b = L.pick[0], above = L.pick[1], inbin = L.pick[2];
+    __syncthreads();
+    if (tid == 0) L.cnt[0] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_pool; base += NT) {
+        const int i = base + tid;
+        const uint64_t e = i < n_pool ? cand[i] : 0;
+        const bool p = i < n_pool && (int32_t)(e >> 52) > b;
+        const int32_t pos = wave_append(&L.cnt[0], p);
+        if (p) L.u[pos] = e;
+    }
+    __syncthreads();
+    return finish_from_candidates<NT>(L, above, n_pool, K - above, 44, (uint64_t)b << 52,
+                                      0xFFFull << 52, inbin);
+}
+
 // Exact selection of the row's top-K candidates into L.u[0, n) (unsorted);
 // returns n.
 //
@@ -889,35 +926,7 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
         __syncthreads();
         return select_hist<VEC, NT>(a, r, L, K);
     }
-    if (n_pool == K) {
-        for (int i = tid; i < n_pool; i += NT) L.u[i] = cand[i];
-        __syncthreads();
-        return K;
-    }
-    // first digit: the top 12 bits, histogrammed in the still empty list
-    uint32_t* hist = reinterpret_cast<uint32_t*>(L.u);
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
-    __syncthreads();
-    for (int base = 0; base < n_pool; base += NT) {
-        const int i = base + tid;
-        hist_add(hist, i < n_pool, i < n_pool ? (uint32_t)(cand[i] >> 52) : 0u);
-    }
-    __syncthreads();
-    find_threshold<NT>([&](int b) { return hist[b]; }, K, L.pick, L.wsum);
-    const int32_t b = L.pick[0], above = L.pick[1], inbin = L.pick[2];
-    __syncthreads();
-    if (tid == 0) L.cnt[0] = 0;
-    __syncthreads();
-    for (int base = 0; base < n_pool; base += NT) {
-        const int i = base + tid;
-        const uint64_t e = i < n_pool ? cand[i] : 0;
-        const bool p = i < n_pool && (int32_t)(e >> 52) > b;
-        const int32_t pos = wave_append(&L.cnt[0], p);
-        if (p) L.u[pos] = e;
-    }
-    __syncthreads();
-    return finish_from_candidates<NT>(L, above, n_pool, K - above, 44, (uint64_t)b << 52,
-                                      0xFFFull << 52, inbin);
+    return resolve_pool<NT>(L, n_pool, K);
 }
 
 template <bool VEC, int NT>
@@ -931,65 +940,125 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     if (!a.always_final && a.tile_begin > 0 && count <= a.tile_begin) return;
     const bool final_out = a.always_final || count <= a.tile_end;
     const int32_t K = a.topk;
-
-    if (a.part_span > 0) {
-        // stage A: the best K of one column partition
-        const int32_t p = blockIdx.y;
-        const int32_t c0 = r.lo + p * a.part_span;
-        const int32_t c1 = min(r.hi, c0 + a.part_span);
-        r.lo = c0;
-        r.hi = max(c0, c1);
-        const int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
-        __syncthreads();
-        sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
-        const int64_t o = r.y * (int64_t)a.run_stride + (int64_t)p * K;
-        for (int j = tid; j < K; j += NT) {
-            int32_t id = -1;
-            float v = __builtin_nanf("");
-            if (j < n_sel) {
-                const uint64_t cc = L.u[j];
-                id = (int32_t)(0xFFFFFFFFu - (uint32_t)cc);
-                v = key_score((uint32_t)(cc >> 32));
-            }
-            a.run_idx[o + j] = id;
-            a.run_val[o + j] = v;
-        }
-        if (tid == 0) a.part_cnt[r.y * gridDim.y + p] = r.hi - r.lo;
-        return;
-    }
-
-    // stage B merges the partial lists (prior) without the score columns
-    const int32_t col_lo = r.lo, col_hi = r.hi;
-    if (a.parts > 0) r.hi = r.lo;
-    int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
+    const int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
     __syncthreads();
-    // (block-select output is ordered by block index: write_row sorts it)
+    // (block-select output is ordered by block index: write_row does that)
     if (!a.blockselect) sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
-    if (a.parts > 0) {
-        // exact iff every truncated partition's last kept candidate ranks
-        // no higher than the merged k-th (dropped candidates rank below it)
-        if (tid == 0) L.cnt[0] = 0;
-        __syncthreads();
-        const uint64_t kth = n_sel == K ? L.u[K - 1] : 0;
-        const int32_t n = prior_len(a);
-        for (int p = tid; p < a.parts; p += NT) {
-            if (a.part_cnt[r.y * a.parts + p] > a.part_k) {
-                const int64_t o = r.y * (int64_t)n + (int64_t)p * a.part_k + a.part_k - 1;
-                const uint64_t cut = composite(score_key(a.prior_val[o]), a.prior_idx[o]);
-                if (n_sel < K || cut > kth) L.cnt[0] = 1;
-            }
-        }
-        __syncthreads();
-        if (L.cnt[0]) {
-            r.prior = false;
-            r.lo = col_lo;
-            r.hi = col_hi;
-            __syncthreads();
-            n_sel = select_core<VEC, NT>(a, r, L, K);
-            __syncthreads();
-            sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
-        }
+    write_row<NT>(a, r, L, n_sel, final_out);
+}
+
+// ------------------------------------------- few long rows over every CU
+//
+// With fewer rows than CUs, one workgroup per row leaves most of the chip
+// idle.  The prefilter then runs as three kernels: (1) one workgroup per
+// row draws the sample and stores the row's key threshold; (2) workgroups
+// over (row, column partition) append every candidate at or above it to
+// the row's pool in global memory (gathered in LDS first, then one atomic
+// per workgroup on the row's counter reserves their run); (3) one workgroup per row loads the pool and resolves it
+// exactly in LDS -- or, when the pool came out too small or overflowed,
+// selects from the whole row with the full histogram path.  Only rows
+// without a prior list take this path.
+
+constexpr uint32_t kNoTau = 0xFFFFFFFFu;  // no usable threshold: stage 3 scans the row
+constexpr int32_t kFilterSpan = 4096;     // columns per filter workgroup
+
+struct PrefilterWs {
+    uint32_t* tau;    // [rows]
+    int32_t* count;   // [rows]
+    uint64_t* pool;   // [rows, kCap]
+};
+
+__host__ __device__ inline PrefilterWs prefilter_ws(void* ws, int64_t n_rows) {
+    char* p = static_cast<char*>(ws);
+    PrefilterWs w;
+    w.pool = reinterpret_cast<uint64_t*>(p);
+    w.tau = reinterpret_cast<uint32_t*>(p + n_rows * kCap * 8);
+    w.count = reinterpret_cast<int32_t*>(p + n_rows * kCap * 8 + n_rows * 4);
+    return w;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void prefilter_sample_kernel(SelectArgs a, int64_t n_rows, PrefilterWs w) {
+    __shared__ SelectLds L;
+    if ((int64_t)blockIdx.x >= n_rows) return;
+    RowCtx r;
+    int32_t count;
+    setup_row<NT>(a, r, L, blockIdx.x, count);
+    const int32_t n = max(0, r.hi - r.lo);
+    uint32_t tau = 0;  // a row that fits the pool keeps every candidate
+    if (n > kCap) {
+        const int32_t K = a.topk;
+        if (!sample_threshold<NT>(a, r, L, n, K + K / 2 - K / 10 + 32, tau)) tau = kNoTau;
     }
+    if (threadIdx.x == 0) {
+        w.tau[r.y] = tau;
+        w.count[r.y] = 0;
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void prefilter_filter_kernel(SelectArgs a, int64_t n_rows, int32_t span,
+                                                               PrefilterWs w) {
+    const int64_t y = blockIdx.x;
+    if (y >= n_rows) return;
+    const uint32_t tau = w.tau[y];
+    if (tau == kNoTau) return;
+    RowCtx r;
+    r.y = y;
+    r.t = a.rows.query(y);
+    r.n_tok = a.vis.tokens(r.t);
+    const int32_t count = a.row_len ? a.row_len[y] : a.vis.count(r.t);
+    r.prior = false;
+    r.srow = a.scores + y * a.score_stride;
+    r.blk_row = nullptr;
+    const int32_t lo = a.col_lo, hi = min(a.n_cols, max(0, count - a.col_key0));
+    r.lo = lo + (int32_t)blockIdx.y * span;
+    r.hi = min(hi, r.lo + span);
+    if (r.lo >= r.hi) return;
+    // gather the partition's hits in LDS, then reserve their run of the
+    // row's pool with one global atomic
+    __shared__ uint64_t buf[kFilterSpan];
+    __shared__ int32_t n_hit, base;
+    if (threadIdx.x == 0) n_hit = 0;
+    __syncthreads();
+    auto f = [&](bool valid, uint32_t key, int32_t idx) {
+        const bool p = valid && key >= tau;
+        const int32_t pos = wave_append(&n_hit, p);
+        if (p) buf[pos] = composite(key, idx);
+    };
+    visit_columns<VEC, 256>(a, r, r.lo, r.hi, f);
+    __syncthreads();
+    if (threadIdx.x == 0) base = atomicAdd(w.count + y, n_hit);
+    __syncthreads();
+    uint64_t* pool = w.pool + y * kCap;
+    for (int i = threadIdx.x; i < n_hit; i += 256)
+        if (base + i < kCap) pool[base + i] = buf[i];
+}
+
+template <bool VEC, int NT>
+__global__ __launch_bounds__(NT) void prefilter_finish_kernel(SelectArgs a, int64_t n_rows, PrefilterWs w) {
+    __shared__ SelectLds L;
+    const int tid = threadIdx.x;
+    if ((int64_t)blockIdx.x >= n_rows) return;
+    RowCtx r;
+    int32_t count;
+    setup_row<NT>(a, r, L, blockIdx.x, count);
+    const bool final_out = a.always_final || count <= a.tile_end;
+    const int32_t K = a.topk;
+    const uint32_t tau = w.tau[r.y];
+    const int32_t n_pool = w.count[r.y];
+    int32_t n_sel;
+    if (tau != kNoTau && ((tau == 0u && n_pool <= K) || (n_pool >= K && n_pool <= kCap))) {
+        const uint64_t* src = w.pool + r.y * kCap;
+        uint64_t* dst = n_pool <= K ? L.u : &L.u[kMaxK];
+        for (int i = tid; i < n_pool; i += NT) dst[i] = src[i];
+        __syncthreads();
+        n_sel = n_pool <= K ? n_pool : resolve_pool<NT>(L, n_pool, K);
+    } else {
+        n_sel = select_hist<VEC, NT>(a, r, L, K);
+    }
+    __syncthreads();
+    sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
@@ -1018,57 +1087,38 @@ hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream
 }
 
 SelectSplit select_split(int64_t n_rows, int32_t n_cols, int32_t topk) {
-    SelectSplit sp{0, 0, 0};
-    constexpr int32_t span = 4096;
-    // one 1024-thread workgroup per row keeps up with rows up to ~64K
-    // candidates; longer rows spread over several CUs
-    if (n_rows <= 0 || n_rows >= 512 || n_cols < 32 * span) return sp;
-    const int32_t parts = (n_cols + span - 1) / span;
-    // twice the expected share of each partition, as a power of two
-    int32_t kp = 64;
-    while (kp < 2 * ((topk + parts - 1) / parts)) kp <<= 1;
-    kp = std::min(kp, topk);
-    if ((int64_t)parts * kp < topk) return sp;
-    sp.parts = parts;
+    SelectSplit sp{0, 0};
+    constexpr int32_t span = kFilterSpan;
+    // fewer rows than CUs and rows long enough for the prefilter
+    if (n_rows <= 0 || n_rows >= 256 || n_cols < kPrefilterMin || topk > kMaxK) return sp;
+    sp.parts = (n_cols + span - 1) / span;
     sp.span = span;
-    sp.part_k = kp;
     return sp;
 }
 
 size_t select_split_workspace(int64_t n_rows, const SelectSplit& sp) {
     if (sp.parts == 0) return 0;
-    const int64_t list = n_rows * sp.parts * (int64_t)sp.part_k;
-    return (size_t)((list * 8 + n_rows * sp.parts * 4 + 255) / 256 * 256);
+    return (size_t)((n_rows * (kCap * 8 + 8) + 255) / 256 * 256);
 }
 
 hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const SelectSplit& sp,
                                void* ws, hipStream_t stream) {
     if (n_rows <= 0) return hipSuccess;
-    const int64_t list = n_rows * sp.parts * (int64_t)sp.part_k;
-    float* pv = static_cast<float*>(ws);
-    int32_t* pi = reinterpret_cast<int32_t*>(pv + list);
-    int32_t* pc = pi + list;
-    SelectArgs sa = a;  // stage A
-    sa.topk = sp.part_k;
-    sa.part_span = sp.span;
-    sa.run_stride = sp.parts * sp.part_k;
-    sa.run_val = pv;
-    sa.run_idx = pi;
-    sa.part_cnt = pc;
-    sa.prior_val = nullptr;
-    sa.prior_idx = nullptr;
-    sa.always_final = 1;
-    launch_nt<256>(sa, n_rows, dim3((unsigned)n_rows, (unsigned)sp.parts), stream);
-    SelectArgs sb = a;  // stage B
-    sb.prior_val = pv;
-    sb.prior_idx = pi;
-    sb.prior_len = sp.parts * sp.part_k;
-    sb.tile_begin = 1;  // use the prior list
-    sb.always_final = 1;
-    sb.parts = sp.parts;
-    sb.part_k = sp.part_k;
-    sb.part_cnt = pc;
-    launch_nt<1024>(sb, n_rows, dim3((unsigned)n_rows), stream);
+    if (a.blocks_mode || (a.prior_val && a.tile_begin > 0))
+        return hipErrorInvalidValue;  // planned for contiguous rows without a prior list only
+    const PrefilterWs w = prefilter_ws(ws, n_rows);
+    hipLaunchKernelGGL((prefilter_sample_kernel<1024>), dim3((unsigned)n_rows), dim3(1024), 0, stream, a,
+                       n_rows, w);
+    const dim3 g2((unsigned)n_rows, (unsigned)sp.parts);
+    if (vec_ok(a)) {
+        hipLaunchKernelGGL((prefilter_filter_kernel<true>), g2, dim3(256), 0, stream, a, n_rows, sp.span, w);
+        hipLaunchKernelGGL((prefilter_finish_kernel<true, 1024>), dim3((unsigned)n_rows), dim3(1024), 0,
+                           stream, a, n_rows, w);
+    } else {
+        hipLaunchKernelGGL((prefilter_filter_kernel<false>), g2, dim3(256), 0, stream, a, n_rows, sp.span, w);
+        hipLaunchKernelGGL((prefilter_finish_kernel<false, 1024>), dim3((unsigned)n_rows), dim3(1024), 0,
+                           stream, a, n_rows, w);
+    }
     return hipGetLastError();
 }
 

@@ -66,20 +66,6 @@ struct SelectArgs {
     int32_t blockselect;
     uint32_t force_flags;
     int32_t sel_block;        // block size (local block = (tokens - 1) / sel_block)
-    // two-stage selection of few long rows.  Stage A (part_span > 0):
-    // workgroup (row, p) keeps the topk best of columns [p * part_span,
-    // (p + 1) * part_span) in run_val / run_idx at row stride run_stride,
-    // offset p * topk, and its candidate count in part_cnt[row * parts + p].
-    // Stage B (parts > 0): the prior list of length prior_len holds those
-    // partial lists; the merged result is checked against every truncated
-    // partition's cutoff and recomputed from the score row when the check
-    // fails.
-    int32_t part_span;
-    int32_t run_stride;
-    int32_t* part_cnt;
-    int32_t prior_len;        // 0: topk
-    int32_t parts;
-    int32_t part_k;
 };
 
 struct PoolArgs {
@@ -92,14 +78,15 @@ struct PoolArgs {
 hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
                         hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream);
-// Two-stage selection plan for a chunk: partitions and partial list length
-// (parts = 0: use the one-workgroup-per-row selection).
+// Selection plan for few long rows (parts = 0: one workgroup per row).
+// parts > 0: a sampled threshold per row, a filter over parts x span column
+// partitions into a per-row pool, and an exact finish per row.
 struct SelectSplit {
-    int32_t parts, span, part_k;
+    int32_t parts, span;
 };
 SelectSplit select_split(int64_t n_rows, int32_t n_cols, int32_t topk);
 size_t select_split_workspace(int64_t n_rows, const SelectSplit& sp);
-// Launch both stages; `ws` holds select_split_workspace bytes.
+// Launch the three kernels; `ws` holds select_split_workspace bytes.
 hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const SelectSplit& sp,
                                void* ws, hipStream_t stream);
 hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
