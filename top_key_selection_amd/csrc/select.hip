@@ -1001,8 +1001,9 @@ __global__ __launch_bounds__(256) void prefilter_filter_kernel(SelectArgs a, int
                                                                PrefilterWs w) {
     const int64_t y = blockIdx.x;
     if (y >= n_rows) return;
+    // (kNoTau passes no finite score, so such a row appends nothing; the
+    // score loads need not wait for the threshold)
     const uint32_t tau = w.tau[y];
-    if (tau == kNoTau) return;
     RowCtx r;
     r.y = y;
     r.t = a.rows.query(y);
