@@ -89,16 +89,17 @@ __device__ __forceinline__ int32_t column_index(const SelectArgs& a, const RowCt
 template <bool VEC, int NT, class F>
 __device__ __forceinline__ void visit_columns(const SelectArgs& a, const RowCtx& r, int32_t c_begin,
                                      int32_t c_end, F&& f) {
-    constexpr int U = 4;
+    constexpr int U = VEC ? 4 : 2;  // (scalar loads need more registers)
+    constexpr int32_t kStep = 4 * NT * U;
     const int tid = threadIdx.x;
     if (c_begin >= c_end) return;
     const int32_t base0 = c_begin & ~3;
     // aligned groups past the end re-read the last group (inside the row's
     // storage, whose stride is a multiple of 4): the vector loads need no
-    // branch, so all U of them stay in flight together
+    // branch, so all U of them stay in flight together, and the next group
+    // of U is loaded before the current one is processed
     const int32_t last = (c_end - 1) & ~3;
-    for (int32_t base = base0; base < c_end; base += 4 * NT * U) {
-        float v[U][4];
+    auto load = [&](float (*v)[4], int32_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int32_t j0 = base + 4 * (u * NT + tid);
@@ -113,6 +114,8 @@ __device__ __forceinline__ void visit_columns(const SelectArgs& a, const RowCtx&
                 }
             }
         }
+    };
+    auto visit = [&](float (*v)[4], int32_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -123,6 +126,15 @@ __device__ __forceinline__ void visit_columns(const SelectArgs& a, const RowCtx&
                 f(idx >= 0, score_key(v[u][i]), idx);
             }
         }
+    };
+    float va[U][4], vb[U][4];
+    load(va, base0);
+    for (int32_t base = base0; base < c_end; base += 2 * kStep) {
+        load(vb, base + kStep);
+        visit(va, base);
+        if (base + kStep >= c_end) break;
+        load(va, base + 2 * kStep);
+        visit(vb, base + kStep);
     }
 }
 
