@@ -40,6 +40,7 @@ constexpr int kCap = 4096;          // LDS candidate list (entries of the thresh
 constexpr int kBins = 4096;         // 12-bit first digit
 constexpr int kBinShift = 20;
 constexpr int kSamples = 2048;      // candidates sampled for the prefilter threshold
+static_assert(kSamples % 256 == 0 && kSamples % 1024 == 0, "whole samples per thread");
 constexpr int kPrefilterMin = 16384; // rows at least this long take the prefilter
 constexpr int kMaxBlkEntries = 512;
 constexpr int kBitmapWords = 4096;  // block-select bitmap (ids below 131072)
@@ -135,6 +136,87 @@ __device__ __forceinline__ void visit_columns(const SelectArgs& a, const RowCtx&
         if (base + kStep >= c_end) break;
         load(va, base + 2 * kStep);
         visit(vb, base + kStep);
+    }
+}
+
+// Append every candidate of columns [c_begin, c_end) whose key is at least
+// tau to dst (slots past cap are counted but not written).  The same
+// double-buffered loads as visit_columns; the appends are batched per
+// thread group of U * 4 columns: each lane counts its hits, a bitwise
+// ballot prefix gives every lane its offset, and one atomic per wave and
+// group reserves the run.
+template <bool VEC, int NT>
+__device__ __forceinline__ void collect_ge(const SelectArgs& a, const RowCtx& r, int32_t c_begin,
+                                           int32_t c_end, uint32_t tau, int32_t* counter,
+                                           uint64_t* dst, int32_t cap) {
+    constexpr int U = VEC ? 4 : 2;
+    constexpr int E = U * 4;
+    constexpr int32_t kStep = 4 * NT * U;
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (c_begin >= c_end) return;
+    const int32_t base0 = c_begin & ~3;
+    const int32_t last = (c_end - 1) & ~3;
+    auto load = [&](float (*v)[4], int32_t base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j0 = base + 4 * (u * NT + tid);
+            if (VEC) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(r.srow + min(j0, last));
+                v[u][0] = x[0]; v[u][1] = x[1]; v[u][2] = x[2]; v[u][3] = x[3];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int32_t j = j0 + i;
+                    v[u][i] = (j >= c_begin && j < c_end) ? r.srow[j] : 0.0f;
+                }
+            }
+        }
+    };
+    const uint64_t lt = (1ull << lane) - 1ull;
+    auto group = [&](float (*v)[4], int32_t base) {
+        uint32_t key[E];
+        int32_t idx[E];
+        int32_t cnt = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t j = base + 4 * (u * NT + tid) + i;
+                const int32_t id = (j >= c_begin && j < c_end) ? column_index(a, r, j) : -1;
+                const uint32_t k = score_key(v[u][i]);
+                const bool p = id >= 0 && k >= tau;
+                key[u * 4 + i] = k;
+                idx[u * 4 + i] = p ? id : -1;
+                cnt += p ? 1 : 0;
+            }
+        }
+        int32_t pre = 0, tot = 0;
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {  // cnt <= 16
+            const uint64_t bb = __ballot((cnt >> b) & 1);
+            pre += __popcll(bb & lt) << b;
+            tot += __popcll(bb) << b;
+        }
+        if (tot == 0) return;
+        int32_t at = 0;
+        if (lane == 0) at = atomicAdd(counter, tot);
+        int32_t pos = __builtin_amdgcn_readlane(at, 0) + pre;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (idx[e] >= 0) {
+                if (pos < cap) dst[pos] = composite(key[e], idx[e]);
+                ++pos;
+            }
+        }
+    };
+    float va[U][4], vb[U][4];
+    load(va, base0);
+    for (int32_t base = base0; base < c_end; base += 2 * kStep) {
+        load(vb, base + kStep);
+        group(va, base);
+        if (base + kStep >= c_end) break;
+        load(va, base + 2 * kStep);
+        group(vb, base + kStep);
     }
 }
 
@@ -809,22 +891,29 @@ __device__ __forceinline__ bool sample_threshold(const SelectArgs& a, const RowC
     for (int i = tid; i < kBins; i += NT) hist[i] = 0;
     if (tid == 0) L.cnt[0] = 0;
     __syncthreads();
-    for (int s = tid; s < kSamples; s += NT) {
+    // every sample load is issued before any is used
+    constexpr int PER = kSamples / NT;
+    bool v[PER];
+    float x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int s = tid + i * NT;
         const int32_t q = (int32_t)(((int64_t)s * n) / kSamples);
-        bool v;
-        float x;
         if (q < np) {
-            v = a.prior_idx[r.y * np + q] >= 0;
-            x = a.prior_val[r.y * np + q];
+            v[i] = a.prior_idx[r.y * np + q] >= 0;
+            x[i] = a.prior_val[r.y * np + q];
         } else {
             const int32_t j = r.lo + (q - np);
-            v = column_index(a, r, j) >= 0;
-            x = r.srow[j];
+            v[i] = column_index(a, r, j) >= 0;
+            x[i] = r.srow[j];
         }
-        const uint32_t key = v ? score_key(x) : 0u;
-        keys[s] = key;
-        hist_add(hist, v, key >> kBinShift);
-        const uint64_t m = __ballot(v);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const uint32_t key = v[i] ? score_key(x[i]) : 0u;
+        keys[tid + i * NT] = key;
+        hist_add(hist, v[i], key >> kBinShift);
+        const uint64_t m = __ballot(v[i]);
         if ((threadIdx.x & 63) == 0 && m) atomicAdd(&L.cnt[0], (int32_t)__popcll(m));
     }
     __syncthreads();
@@ -924,7 +1013,7 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
         if (p && pos < cap) dst[pos] = composite(key, idx);
     };
     visit_prior<NT>(a, r, c);
-    visit_columns<VEC, NT>(a, r, r.lo, r.hi, c);
+    collect_ge<VEC, NT>(a, r, r.lo, r.hi, tau, &L.cnt[1], dst, cap);
     __syncthreads();
     const int32_t n_pool = L.cnt[1];
     if (direct) return n_pool;
@@ -1034,12 +1123,7 @@ __global__ __launch_bounds__(256) void prefilter_filter_kernel(SelectArgs a, int
     __shared__ int32_t n_hit, base;
     if (threadIdx.x == 0) n_hit = 0;
     __syncthreads();
-    auto f = [&](bool valid, uint32_t key, int32_t idx) {
-        const bool p = valid && key >= tau;
-        const int32_t pos = wave_append(&n_hit, p);
-        if (p) buf[pos] = composite(key, idx);
-    };
-    visit_columns<VEC, 256>(a, r, r.lo, r.hi, f);
+    collect_ge<VEC, 256>(a, r, r.lo, r.hi, tau, &n_hit, buf, kFilterSpan);
     __syncthreads();
     if (threadIdx.x == 0) base = atomicAdd(w.count + y, n_hit);
     __syncthreads();
