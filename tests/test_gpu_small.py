@@ -251,6 +251,28 @@ def test_shared_key_hisa_prefill_exact():
                       "shared hisa")
 
 
+def test_tied_running_list_across_tiles_keeps_lowest_indices():
+    """Scores tied at the k-th place across key tiles: the running list of
+    earlier tiles carries the tie group, and the later tiles' selection must
+    still keep the lowest indices (the running list is not kept sorted
+    between tiles)."""
+    say("ties across tiles with a running list")
+    n_k, K = 9000, 2048
+    q = np.zeros((1, 3, 1, 32), np.float32)
+    q[..., 0] = 1.0                                    # score = relu(k[s, 0])
+    w = np.ones((1, 3, 1), np.float32)
+    kv = np.zeros((1, n_k, 32), np.float32)
+    hot = np.array([4500, 4501, 5000, 7000, 8999, 6000, 6001, 6002, 4096, 8192])
+    kv[0, hot, 0] = 1.0
+    kv[0, hot[:3], 0] = 2.0
+    x = dict(q=fp32_to_bf16_bits(q), w=w, k=fp32_to_bf16_bits(kv), k_scale=None)
+    sh = dict(batch=1, n_q=3, n_k=n_k, heads=1, dim=32, q_pos0=n_k - 3, causal_ratio=1, key_dtype=0)
+    oi, ov = oracle_flat(sh, x, K)
+    for kt in (0, 4096, 2048, 1024):
+        gi, gv = gpu_flat(sh, x, K, 0, kt)
+        assert_topk_exact(gi, gv, oi, ov, "ties k_tile=%d" % kt)
+
+
 def test_fp8_keys_integer_exact():
     say("fp8 keys, integer codes, power-of-two scales")
     sh, x = int_case(28, batch=2, n_q=64, n_k=1100, heads=8, dim=128, q_pos0=1036, fp8=True)

@@ -698,8 +698,41 @@ __device__ __forceinline__ int32_t radix_fallback(const SelectArgs& a, const Row
         eq_base += tot;
         __syncthreads();
     };
-    // ordered scan: one candidate per thread per round (scalar) keeps order
-    if (r.prior) visit_prior<NT>(a, r, g);
+    // The prior list holds keys below every column's index, but in no
+    // particular order: its tied entries are gathered, and when they are
+    // more than needed, the ones with the lowest indices are picked by a
+    // sort (a composite of equal keys orders by index alone).
+    if (r.prior) {
+        uint64_t* tie = &L.u[kMaxK];  // the histograms are done with
+        if (tid == 0) L.cnt[1] = 0;
+        __syncthreads();
+        auto gp = [&](bool valid, uint32_t key, int32_t idx) {
+            bool gt = false, eq = false;
+            if (valid) {
+                if (take_all || shift_done >= 32) {
+                    gt = take_all;
+                } else {
+                    const uint32_t hi = key >> shift_done;
+                    gt = hi > pb;
+                    eq = hi == pb;
+                }
+            }
+            const int32_t pos = wave_append(&L.cnt[0], gt);
+            if (gt && pos < K) L.u[pos] = composite(key, idx);
+            const int32_t pe = wave_append(&L.cnt[1], eq);
+            if (eq) tie[pe] = composite(key, idx);
+        };
+        visit_prior<NT>(a, r, gp);
+        __syncthreads();
+        const int32_t n_tie = L.cnt[1];
+        if (n_tie > need) sort_desc<NT>(tie, &L.u[kMaxK + kMaxK], n_tie);
+        const int32_t take = min(n_tie, need);
+        for (int i = tid; i < take; i += NT) L.u[n_gt + i] = tie[i];
+        eq_base = take;
+        __syncthreads();
+    }
+    // ordered scan of the columns: one candidate per thread per round
+    // (scalar) keeps index order
     {
         RowCtx rr = r;
         for (int32_t base = r.lo; base < r.hi; base += NT) {
@@ -1043,8 +1076,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     const int32_t K = a.topk;
     const int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
     __syncthreads();
-    // (block-select output is ordered by block index: write_row does that)
-    if (!a.blockselect) sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
+    // (block-select output is ordered by block index: write_row does that;
+    // the running list of a non-final tile needs no order)
+    if (!a.blockselect && final_out) sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
