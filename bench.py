@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-topk-standalone", action="store_true",
+                    help="skip the selection-only measurement on a 1 GiB score matrix")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -330,6 +332,31 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, k_np, ks_np, nvis, args.cpu_seconds)
 
+    # ---- the selection on its own over a materialised 1 GiB fp32 score
+    # matrix (4096 rows x 65536 keys): 4 B read per score, 8 B written per
+    # output entry (index + value)
+    ts = None
+    if not args.no_topk_standalone:
+        g = torch.Generator(device=dev).manual_seed(12345)
+        sc = torch.randn((4096, 65536), device=dev, generator=g)
+        t_idx = torch.empty((4096, K), dtype=torch.int32, device=dev)
+        t_val = torch.empty((4096, K), dtype=torch.float32, device=dev)
+        t_ws = tks.workspace(tks.topk_scores_workspace(4096, 65536, K), dev)
+        for _ in range(2):
+            tks.topk_scores(sc, K, ws=t_ws, idx=t_idx, vals=t_val)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(5):
+            tks.topk_scores(sc, K, ws=t_ws, idx=t_idx, vals=t_val)
+        e1.record()
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1) / 5
+        tb = sc.numel() * 4 + 4096 * K * 8
+        ts = dict(rows=4096, keys=65536, k=K, ms=round(t_ms, 4),
+                  gb_per_s=round(tb / (t_ms * 1e-3) / 1e9, 1),
+                  frac_hbm=round(tb / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        del sc, t_idx, t_val, t_ws
+
     line = {
         "metric": METRIC, "value": value, "unit": "q-k scores/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -341,6 +368,7 @@ def main():
         "cpu_baseline": cpu,
         **out,
         "kernels": kern,
+        "topk_standalone": ts,
     }
     print(json.dumps(line), flush=True)
 

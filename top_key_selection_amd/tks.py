@@ -176,7 +176,11 @@ def topk_flat(shape: Shape, q, w, k, k_scale, topk, q_chunk=0, k_tile=0, with_va
     return idx, vals
 
 
-def topk_scores(scores, topk, row_len=None, with_vals=True):
+def topk_scores_workspace(n_rows, n_cols, topk) -> int:
+    return int(lib().tks_topk_scores_workspace(n_rows, n_cols, topk))
+
+
+def topk_scores(scores, topk, row_len=None, with_vals=True, ws=None, idx=None, vals=None):
     """Top-k of each row of an fp32 [n_rows, n_cols] (row-strided) score matrix."""
     _dev(scores, "scores", (torch.float32,)) if scores.is_contiguous() else None
     if scores.dim() != 2 or scores.stride(1) != 1:
@@ -184,10 +188,16 @@ def topk_scores(scores, topk, row_len=None, with_vals=True):
     n_rows, n_cols = scores.shape
     _dev(row_len, "row_len", (torch.int32,))
     dev = scores.device
-    idx = torch.empty((n_rows, topk), dtype=torch.int32, device=dev)
-    vals = torch.empty((n_rows, topk), dtype=torch.float32, device=dev) if with_vals else None
-    need = int(lib().tks_topk_scores_workspace(n_rows, n_cols, topk))
-    ws = workspace(need, dev)
+    if idx is None:
+        idx = torch.empty((n_rows, topk), dtype=torch.int32, device=dev)
+    if vals is None and with_vals:
+        vals = torch.empty((n_rows, topk), dtype=torch.float32, device=dev)
+    _dev(idx, "idx", (torch.int32,)), _dev(vals, "vals", (torch.float32,))
+    for t, name in ((idx, "idx"), (vals, "vals")):
+        if t is not None and t.numel() != n_rows * topk:
+            raise ValueError("%s must hold n_rows x topk = %d elements" % (name, n_rows * topk))
+    if ws is None:
+        ws = workspace(topk_scores_workspace(n_rows, n_cols, topk), dev)
     _check(lib().tks_topk_scores(_p(scores), n_rows, n_cols, scores.stride(0), _p(row_len), topk,
                                  _p(idx), _p(vals), _p(ws), ws.numel(), _stream()))
     return idx, vals
