@@ -122,7 +122,9 @@ int tks_topk_flat(const tks_shape* shape, const void* q, const float* w, const v
  * of a row is key index j.  Scores must not be NaN.
  *   idx / vals: [n_rows, topk] (vals may be NULL).
  *   workspace: tks_topk_scores_workspace(n_rows, n_cols, topk) bytes, 256-byte
- *   aligned (0 -- and NULL accepted -- unless the rows are few and long).
+ *   aligned.  It is 0 (and NULL is accepted) unless the rows are fewer than
+ *   256 and at least 16384 long; such rows are spread over every CU through
+ *   a per-row candidate pool of 32 KiB in the workspace.
  */
 size_t tks_topk_scores_workspace(int32_t n_rows, int32_t n_cols, int32_t topk);
 int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t row_stride,

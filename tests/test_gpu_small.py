@@ -362,8 +362,8 @@ def test_topk_scores_matches_full_sort(n_cols, topk):
     sc[2] = -0.0
     sc[3] = rng.standard_normal(n_cols).astype(np.float32)
     sc[4, ::2] = -np.inf
-    # the k best all in one column partition: the two-stage selection for few
-    # long rows must detect the truncated partition and recompute exactly
+    # the k best all in one column partition (few long rows are filtered
+    # partition by partition into one pool per row)
     sc[5] = np.arange(n_cols, dtype=np.float32)
     sc[6] = -np.arange(n_cols, dtype=np.float32)
     sc[7] = np.where(np.arange(n_cols) % 3 == 0, 5.0, rng.standard_normal(n_cols)).astype(np.float32)

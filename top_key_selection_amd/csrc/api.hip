@@ -140,7 +140,7 @@ struct FlatPlan {
     int32_t q_chunk;
     int32_t k_tile;
     int64_t score_stride;
-    tks::SelectSplit split;  // two-stage selection of few long rows (one tile)
+    tks::SelectSplit split;  // few long rows over every CU (single tile only)
     size_t off_scores, off_run_val, off_run_idx, off_split, bytes;
 };
 
