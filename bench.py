@@ -175,9 +175,23 @@ def main():
             if marks is not None:
                 marks[3].record()
 
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # HBM: what the step holds (inputs, outputs, workspaces; the library
+    # allocates nothing) against the fp32 score tensors it never builds
+    nbytes = lambda *ts: int(sum(t.numel() * t.element_size() for t in ts if t is not None))
+    mem = dict(inputs=nbytes(q, w, k, ks), outputs=nbytes(f_idx, f_val),
+               workspace=nbytes(f_ws))
+    if hisa:
+        mem["outputs"] += nbytes(pooled, blk, h_idx, h_val)
+        mem["workspace"] += nbytes(b_ws, r_ws)
+    mem["peak_allocated"] = int(torch.cuda.max_memory_allocated(dev))
+    mem["materialised_scores_fp32"] = cfg.batch * cfg.n_q * cfg.n_k * 4
+    mem["materialised_head_scores_fp32"] = tks.materialized_score_bytes(cfg.batch, cfg.n_q, cfg.heads,
+                                                                         cfg.n_k)
 
     # ---- timed region: K steps, events between the calls
     marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
@@ -368,6 +382,7 @@ def main():
         "cpu_baseline": cpu,
         **out,
         "kernels": kern,
+        "hbm_bytes": mem,
         "topk_standalone": ts,
     }
     print(json.dumps(line), flush=True)
