@@ -58,6 +58,9 @@ def lib():
         L.orc_e4m3fn_to_double.restype = ctypes.c_double
         L.orc_double_to_bf16.argtypes = [ctypes.c_double]
         L.orc_double_to_bf16.restype = ctypes.c_uint16
+        L.orc_float_to_e4m3fn.argtypes = [ctypes.c_float]
+        L.orc_float_to_e4m3fn.restype = ctypes.c_uint8
+        L.orc_compress_keys.argtypes = [SP, P, i64, P, P]
         L.orc_n_visible.argtypes = [SP, i64]
         L.orc_n_visible.restype = i64
         L.orc_index_scores.argtypes = [SP, P, P, P, P, i32, i32, i32, i32, P]
@@ -107,6 +110,10 @@ def e4m3fn_to_double(code: int) -> float:
 
 def double_to_bf16(x: float) -> int:
     return int(lib().orc_double_to_bf16(float(x)))
+
+
+def float_to_e4m3fn(x: float) -> int:
+    return int(lib().orc_float_to_e4m3fn(float(x)))
 
 
 def n_visible(shape: dict, t: int) -> int:
@@ -206,3 +213,20 @@ def hisa(shape: dict, q_rows, w_rows, k, k_scale, block, m_scored, flags, topk, 
                           _ptr(_c(k_scale, np.float32)), block, m_scored, flags, topk,
                           _ptr(rows), n, _ptr(blk), _ptr(idx), _ptr(val)), "hisa")
     return blk, idx, val
+
+
+def compress_keys(raw, ratio: int, key_fp8: bool, n_k: int | None = None):
+    """Compressed key cache of raw bf16 keys [batch, n_raw, dim] at ratio m.
+
+    Returns (k, k_scale): k is [batch, n_k, dim] bf16 bits (uint16) or e4m3fn
+    codes (uint8), k_scale fp32 [batch, n_k] or None; slots from n_raw // m on
+    are zero.  n_k defaults to n_raw // m."""
+    raw = _c(raw, np.uint16)
+    batch, n_raw, dim = raw.shape
+    n_k = n_raw // ratio if n_k is None else n_k
+    S = _shape(batch, 1, n_k, 1, dim, 0, ratio, 1 if key_fp8 else 0)
+    k = np.zeros((batch, n_k, dim), np.uint8 if key_fp8 else np.uint16)
+    ks = np.zeros((batch, n_k), np.float32) if key_fp8 else None
+    _check(lib().orc_compress_keys(ctypes.byref(S), _ptr(raw), n_raw, _ptr(k), _ptr(ks)),
+           "compress_keys")
+    return k, ks

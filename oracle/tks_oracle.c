@@ -37,6 +37,17 @@
  *    only within the retained blocks): flat top-k over the visible keys whose
  *    block is kept.
  *
+ *  - Key compression (StreamIndex abstract: the indexer reads keys
+ *    compressed by a ratio m, m = 4 for V4-Flash): compressed key j is the
+ *    bf16 (nearest-even) rounding of the mean of raw keys m*j .. m*j+m-1,
+ *    summed in double in position order.  An fp8 key cache stores it as
+ *    e4m3fn codes with one fp32 scale per key: scale = max_d |kc[d]| / 448
+ *    (fp32 division), code[d] = nearest e4m3fn of kc[d] / scale (fp32
+ *    division; ties to the even code, saturated at 448, sign kept); an
+ *    all-zero key gets scale 0 and zero codes.  The pages give no formula
+ *    for the compressor; this mean is the plainest reading of "compressed
+ *    keys" that the HISA pooling (a block mean) also uses.
+ *
  * Errors: a function returns 0 on success and a negative value on a bad
  * argument; outputs are then untouched.
  */
@@ -108,6 +119,28 @@ uint16_t orc_double_to_bf16(double x) {
         }
     }
     return (uint16_t)(out | (neg ? 0x8000 : 0));
+}
+
+/* OCP e4m3fn code of x: the nearest e4m3fn magnitude to |x| (saturated at
+ * 448, the largest finite one), ties to the even code, sign bit copied.
+ * Magnitudes below 2^-6 lie on the subnormal grid of step 2^-9; a normal
+ * magnitude 1.m * 2^E (-6 <= E <= 8) on the grid of step 2^(E-3).  A value
+ * rounding up to the next power of two lands on that binade's first code,
+ * which the grid index gives by itself. */
+uint8_t orc_float_to_e4m3fn(float x) {
+    double a = fabs((double)x);
+    if (a > 448.0) a = 448.0;
+    int code;
+    if (a < ldexp(1.0, -6)) {
+        code = (int)rint(a / ldexp(1.0, -9)); /* 0 .. 8; 8 is 2^-6, code 0x08 */
+    } else {
+        int ex;
+        frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1): E = ex - 1 */
+        int E = ex - 1;
+        int n = (int)rint(a / ldexp(1.0, E - 3)); /* 8 .. 16 significand steps */
+        code = ((E + 7) << 3) + (n - 8);         /* n = 16 carries into E + 1 */
+    }
+    return (uint8_t)(code | (signbit(x) ? 0x80 : 0));
 }
 
 /* --------------------------------------------------------------- geometry */
@@ -455,6 +488,48 @@ int orc_hisa(const orc_shape* S, const uint16_t* q, const float* w, const void* 
         rc = orc_refine(S, q, w, k, k_scale, block, blk, m_total, topk, rows, n_rows, idx, val);
     free(pooled);
     return rc;
+}
+
+/* ------------------------------------------------------- key compression */
+
+/* Compress raw bf16 keys [batch, n_raw, dim] (ratio m = S->causal_ratio):
+ * the n_raw / m complete groups give keys 0 .. n_raw/m - 1 of the cache
+ * k [batch, S->n_k, dim] (bf16 bits, or e4m3fn codes with k_scale
+ * [batch, S->n_k] when S->key_fp8).  Cache slots past n_raw / m are not
+ * written. */
+int orc_compress_keys(const orc_shape* S, const uint16_t* raw, int64_t n_raw, void* k,
+                      float* k_scale) {
+    if (check_shape(S) || n_raw < 0 || n_raw / S->causal_ratio > S->n_k) return -1;
+    const int64_t m = S->causal_ratio, D = S->dim;
+    const int64_t nc = n_raw / m;
+    const int64_t n = (int64_t)S->batch * nc;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t b = i / nc, j = i % nc;
+        const int64_t out = b * S->n_k + j;
+        uint16_t kc[D];
+        for (int64_t d = 0; d < D; ++d) {
+            double sum = 0.0;
+            for (int64_t r = 0; r < m; ++r)
+                sum += orc_bf16_to_double(raw[(b * n_raw + m * j + r) * D + d]);
+            kc[d] = orc_double_to_bf16(sum / (double)m);
+        }
+        if (!S->key_fp8) {
+            memcpy((uint16_t*)k + out * D, kc, sizeof(uint16_t) * (size_t)D);
+            continue;
+        }
+        float amax = 0.0f;
+        for (int64_t d = 0; d < D; ++d) {
+            float v = fabsf((float)orc_bf16_to_double(kc[d]));
+            if (v > amax) amax = v;
+        }
+        const float scale = amax / 448.0f;
+        const float div = scale > 0.0f ? scale : 1.0f;
+        for (int64_t d = 0; d < D; ++d)
+            ((uint8_t*)k)[out * D + d] = orc_float_to_e4m3fn((float)orc_bf16_to_double(kc[d]) / div);
+        k_scale[out] = scale;
+    }
+    return 0;
 }
 
 int orc_num_threads(void) {

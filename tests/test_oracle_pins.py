@@ -265,7 +265,10 @@ def _nearest_bf16_ok(bits, exact):
     up = bf16_bits_to_fp32((bits.astype(np.int32) + 1).astype(np.uint16)).astype(np.float64)
     dn = bf16_bits_to_fp32((bits.astype(np.int32) - 1).astype(np.uint16)).astype(np.float64)
     err = np.abs(v - exact)
-    return np.all(err <= np.abs(up - exact)) and np.all(err <= np.abs(dn - exact))
+    # the neighbour pattern of +0 (0xFFFF) is NaN: no closer value there
+    d_up = np.where(np.isnan(up), np.inf, np.abs(up - exact))
+    d_dn = np.where(np.isnan(dn), np.inf, np.abs(dn - exact))
+    return np.all(err <= d_up) and np.all(err <= d_dn)
 
 
 def test_pool_of_floats_is_nearest_bf16_of_mean_and_ignores_tail():
@@ -291,6 +294,104 @@ def test_pool_fp8_uses_dequantised_keys():
         scale.astype(np.float64)[..., None]
     exact = deq.reshape(1, T // B, B, D).mean(axis=2)
     assert _nearest_bf16_ok(got, exact)
+
+
+# --------------------------------------------------------- key compression
+# (StreamIndex abstract: the indexer reads keys compressed by a ratio m; the
+# compressed key is read as the bf16 mean of m consecutive raw keys, stored
+# in an fp8 cache as e4m3fn codes with a per-key scale max|kc| / 448.)
+
+def test_e4m3fn_encoder_matches_torch_on_ties_and_random_values():
+    mags = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)   # exact ties
+    rng = np.random.default_rng(30)
+    x = np.concatenate([
+        mags.astype(np.float32), mids,
+        np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000)),
+        rng.uniform(-448, 448, 3000).astype(np.float32),
+        (rng.standard_normal(3000) * 0.01).astype(np.float32),
+    ])
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.float_to_e4m3fn(v) for v in x], np.uint8)
+    np.testing.assert_array_equal(got, ref)
+    # saturation at the largest finite magnitude, 448
+    assert oracle.float_to_e4m3fn(1e6) == 0x7E and oracle.float_to_e4m3fn(-1e6) == 0xFE
+
+
+def test_compress_ratio_one_is_identity_for_bf16_keys():
+    rng = np.random.default_rng(31)
+    raw = fp32_to_bf16_bits(rng.standard_normal((2, 50, 16)).astype(np.float32))
+    k, ks = oracle.compress_keys(raw, 1, False)
+    assert ks is None
+    np.testing.assert_array_equal(k, raw)
+
+
+def test_compress_integer_groups_is_exact_mean_and_drops_the_partial_group():
+    rng = np.random.default_rng(32)
+    raw = rand_int(rng, (2, 4 * 37 + 3, 8), -16, 16)
+    k, _ = oracle.compress_keys(fp32_to_bf16_bits(raw), 4, False)
+    assert k.shape == (2, 37, 8)
+    # group sums lie in [-64, 64], so every mean is a multiple of 1/4 with at
+    # most 7 significant bits: exact in bf16
+    ref = raw[:, :4 * 37].reshape(2, 37, 4, 8).astype(np.float64).mean(axis=2)
+    np.testing.assert_array_equal(bf16_bits_to_fp32(k).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("group,bits", [
+    ([1, 1, 1, 1 + 2 ** -6], 0x3F80),               # mean 1 + 2^-8: tie, even is 1
+    ([1, 1, 1 + 2 ** -6, 1 + 2 ** -5], 0x3F82),     # mean 1 + 3 * 2^-8: tie, even is 1 + 2^-6
+    ([-1, -1, -1, -1 - 2 ** -6], 0xBF80),
+    ([1, 1, 2], 0x3FAB),                            # mean 4/3: nearest is 1 + 43/128
+])
+def test_compress_rounds_the_mean_to_nearest_even_bf16(group, bits):
+    raw = fp32_to_bf16_bits(np.array(group, np.float32).reshape(1, len(group), 1))
+    k, _ = oracle.compress_keys(raw, len(group), False)
+    assert int(k[0, 0, 0]) == bits
+
+
+def test_compress_random_means_are_nearest_bf16():
+    rng = np.random.default_rng(33)
+    raw = fp32_to_bf16_bits(rng.standard_normal((3, 4 * 200, 16)).astype(np.float32))
+    k, _ = oracle.compress_keys(raw, 4, False)
+    exact = bf16_bits_to_fp32(raw).astype(np.float64).reshape(3, 200, 4, 16).mean(axis=2)
+    assert _nearest_bf16_ok(k, exact)
+
+
+def test_fp8_cache_scale_is_max_over_448():
+    # keys whose largest magnitude is 7 = 448 * 2^-6: the scale is exactly
+    # 2^-6 and every integer coordinate times 64 is an exact e4m3fn value
+    rng = np.random.default_rng(35)
+    kc = rand_int(rng, (2, 40, 32), -7, 7)
+    kc[:, :, 3] = 7.0 * np.where(rng.random((2, 40)) < 0.5, 1, -1)
+    kc[1, 5] = 0.0                                  # all-zero key
+    raw = fp32_to_bf16_bits(np.repeat(kc, 4, axis=1))   # constant groups: exact means
+    k8, ks = oracle.compress_keys(raw, 4, True)
+    assert ks[1, 5] == 0.0 and (k8[1, 5] == 0).all()
+    mask = np.ones((2, 40), bool)
+    mask[1, 5] = False
+    assert (ks[mask] == np.float32(2.0 ** -6)).all()
+    deq = torch.from_numpy(k8).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(deq[mask] * 2.0 ** -6, kc[mask])
+
+
+def test_fp8_cache_codes_are_torch_e4m3fn_of_key_over_scale():
+    rng = np.random.default_rng(34)
+    raw = fp32_to_bf16_bits((rng.standard_normal((2, 4 * 64, 32)) * 3).astype(np.float32))
+    kb, _ = oracle.compress_keys(raw, 4, False)
+    k8, ks = oracle.compress_keys(raw, 4, True)
+    kc = bf16_bits_to_fp32(kb)
+    deq = torch.from_numpy(k8).view(torch.float8_e4m3fn).double().numpy()
+    # the largest coordinate of every key maps to +-448
+    assert (np.abs(deq).max(axis=2) == 448.0).all()
+    x = (kc / ks[..., None]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(k8, ref)
+    # dequantised keys within half an e4m3fn step (relative 2^-4, absolute
+    # 2^-10 * scale on the subnormal grid)
+    err = np.abs(deq * ks[..., None] - kc)
+    bound = np.maximum(np.abs(kc) * 2.0 ** -4, ks[..., None] * 2.0 ** -10)
+    assert (err <= bound * (1 + 1e-6)).all()
 
 
 # ----------------------------------------------------------- block selection
