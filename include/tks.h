@@ -143,6 +143,37 @@ int tks_hisa_pool_keys(const tks_shape* shape, const void* k, const float* k_sca
                        int32_t block, void* pooled, hipStream_t stream);
 
 /*
+ * Key-cache append with key compression, fp8 quantisation and block pooling
+ * fused (StreamIndex abstract: the indexer reads keys compressed by a ratio
+ * m; HISA abstract, stage (1): pooled block representatives).  m is
+ * shape->causal_ratio, the key dtype shape->key_dtype, the cache capacity
+ * shape->n_k keys per sequence; n_q, heads and q_pos0 are not used.
+ *
+ * Every sequence's raw key stream already holds raw_len keys; the call
+ * appends raw[b, 0 .. n_new) (bf16 [batch, n_new, dim], 16-byte aligned) to
+ * each sequence b.  Compressed key j is the bf16 nearest-even rounding of
+ * the mean of raw keys m*j .. m*j+m-1 (summed in double in position order);
+ * when its last raw key arrives it is written to k (bf16 [batch, n_k, dim]),
+ * or for fp8 keys as e4m3fn codes of kc / scale (nearest, ties to even,
+ * saturating at 448) with k_scale[b, j] = max_d |kc[d]| / 448 in fp32 (0
+ * and zero codes for an all-zero key).  With block > 0, pooled block J
+ * (bf16 [batch, n_k / block, dim], the value tks_hisa_pool_keys gives from
+ * k) is written when its last compressed key arrives, in the same pass: a
+ * decode step never re-reads the cache to keep the pooled keys current.
+ *   raw_tail: bf16 [batch, m, dim], caller-owned staging of the raw keys of
+ *   a group that is still incomplete after a call; it carries state from
+ *   one call to the next and must not be modified in between (NULL allowed
+ *   when m = 1).  Its content is not read while raw_len is a multiple of m.
+ * Requires raw_len >= 0, n_new >= 0, (raw_len + n_new) / m <= n_k, block 0
+ * or a supported HISA block.  Only the completed keys, their scales, the
+ * completed pooled blocks and the staging slots are written.  Calls that
+ * share raw_tail or overlapping cache slots must be ordered on one stream.
+ */
+int tks_kv_append(const tks_shape* shape, const void* raw, int32_t n_new, int32_t raw_len,
+                  void* raw_tail, void* k, float* k_scale, int32_t block, void* pooled,
+                  hipStream_t stream);
+
+/*
  * HISA block selection (HISA abstract, stage (1): score the pooled block
  * representatives with the indexer and discard irrelevant regions).  For
  * query t with local block L (the block holding its last visible key):
@@ -193,6 +224,7 @@ int tks_hisa_refine_topk(const tks_shape* shape, const void* q, const float* w, 
  *   "select_refine" -- top-k selection of tks_hisa_refine_topk
  *   "select_scores" -- tks_topk_scores
  *   "pool"          -- tks_hisa_pool_keys
+ *   "append"        -- tks_kv_append
  * Returns TKS_EINVAL for an unknown role or NULL outputs.
  */
 int tks_profile_enable(int on);

@@ -137,3 +137,26 @@ def test_hisa_rejects():
     assert ref(64, 0, 4) == EUNSUP
     assert ref(64, 4, 0) == EUNSUP
     assert ref(96, 4, 4) == EUNSUP
+
+
+def test_kv_append_rejects():
+    L = tks.lib()
+
+    def app(s, raw=A, n_new=4, raw_len=0, tail=A, k=A, ks=None, blk=0, pooled=None):
+        return L.tks_kv_append(ctypes.byref(s), raw, n_new, raw_len, tail, k, ks, blk, pooled, None)
+
+    s4 = S(n_k=16, causal_ratio=4)
+    assert app(s4, raw_len=-1) == EINVAL
+    assert app(s4, n_new=-1) == EINVAL
+    assert app(s4, n_new=68) == EINVAL                      # 68 // 4 > 16 keys
+    assert app(s4, raw_len=60, n_new=8) == EINVAL
+    assert "overflows" in tks.last_error()
+    assert app(s4, blk=48) == EUNSUP
+    assert app(s4, blk=64, pooled=None) == EINVAL
+    assert app(s4, raw=None) == EINVAL
+    assert app(s4, raw=MIS) == EINVAL
+    assert app(s4, tail=None) == EINVAL                     # ratio 4 stages raw keys
+    assert app(s4, k=None) == EINVAL
+    assert app(S(n_k=16, key_dtype=1)) == EINVAL            # fp8 cache without scales
+    assert app(s4, n_new=0, raw=None, tail=None, k=None) == tks.OK   # nothing to append
+    assert app(S(batch=0, causal_ratio=4), raw=None, tail=None, k=None) == tks.OK

@@ -33,7 +33,7 @@ KEY_FP8 = 1
 # Rows of the flattened leading dimension drawn from one PCG64 stream.
 ROW_BLOCK = 1024
 
-TENSOR_ID = {"q": 1, "w": 2, "k": 3, "kdrift": 4, "kraw": 5}
+TENSOR_ID = {"q": 1, "w": 2, "k": 3, "kdrift": 4, "kraw": 5, "append": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -255,6 +255,22 @@ def gen_keys(cfg: Config):
         mean = raw.reshape(B, T, m, D).sum(axis=2) / m
         return fp32_to_bf16_bits(mean.astype(np.float32)), None
     raise ValueError(cfg.dist)
+
+
+def gen_raw_keys(seed: int, batch: int, n_raw: int, dim: int, seqs=None) -> np.ndarray:
+    """Raw keys for the key-cache append: bf16 bits of N(0, 1), [len(seqs), n_raw,
+    dim] for the listed sequences (all by default); sequence b comes from its
+    own stream, so a sample of sequences can be drawn alone."""
+    seqs = list(range(batch)) if seqs is None else [int(b) for b in seqs]
+    out = np.empty((len(seqs), n_raw, dim), np.uint16)
+
+    def one(i):
+        g = _rng(seed, "append", seqs[i])
+        out[i] = fp32_to_bf16_bits(g.standard_normal((n_raw, dim), dtype=np.float32))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(len(seqs))))
+    return out
 
 
 def make_inputs(cfg: Config) -> dict:

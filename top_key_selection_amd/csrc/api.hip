@@ -385,6 +385,53 @@ int tks_hisa_pool_keys(const tks_shape* s, const void* k, const float* k_scale, 
     return TKS_OK;
 }
 
+int tks_kv_append(const tks_shape* s, const void* raw, int32_t n_new, int32_t raw_len,
+                  void* raw_tail, void* k, float* k_scale, int32_t block, void* pooled,
+                  hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (raw_len < 0 || n_new < 0) return fail(TKS_EINVAL, "raw_len %d / n_new %d negative", raw_len, n_new);
+    const int64_t m = s->causal_ratio;
+    const int64_t total = (int64_t)raw_len + n_new;
+    if (total / m > s->n_k)
+        return fail(TKS_EINVAL, "append of %d raw keys after %d overflows the cache (%d keys at ratio %d)",
+                    n_new, raw_len, s->n_k, s->causal_ratio);
+    if (block != 0 && block_shift_of(block) < 0)
+        return fail(TKS_EUNSUPPORTED, "block = %d (supported 0, 32, 64, 128, 256)", block);
+    if (s->batch == 0 || n_new == 0) return TKS_OK;
+    if (!raw || !aligned(raw, 16)) return fail(TKS_EINVAL, "raw is NULL or not 16-byte aligned");
+    if (m > 1 && (!raw_tail || !aligned(raw_tail, 16)))
+        return fail(TKS_EINVAL, "raw_tail is NULL or not 16-byte aligned (ratio %d)", s->causal_ratio);
+    if (!k || !aligned(k, 16)) return fail(TKS_EINVAL, "k is NULL or not 16-byte aligned");
+    if (s->key_dtype == TKS_KEY_FP8_E4M3FN && (!k_scale || !aligned(k_scale, 4)))
+        return fail(TKS_EINVAL, "fp8 keys need a 4-byte aligned k_scale");
+    if (block > 0 && (!pooled || !aligned(pooled, 16)))
+        return fail(TKS_EINVAL, "pooled is NULL or not 16-byte aligned");
+    tks::AppendArgs a{};
+    a.raw = static_cast<const uint16_t*>(raw);
+    a.tail = static_cast<uint16_t*>(raw_tail);
+    a.k = k;
+    a.k_scale = k_scale;
+    a.pooled = block > 0 ? static_cast<uint16_t*>(pooled) : nullptr;
+    a.batch = s->batch;
+    a.n_k = s->n_k;
+    a.n_new = n_new;
+    a.m = (int32_t)m;
+    a.raw_len = raw_len;
+    a.g0 = (int32_t)(raw_len / m);
+    a.g1 = (int32_t)(total / m);
+    a.span = block > 0 ? block : 64;
+    a.J0 = a.g0 / a.span;
+    a.n_jobs = std::max<int32_t>(1, (a.g1 + a.span - 1) / a.span - a.J0);
+    hipError_t e;
+    {
+        Timed tm("append", stream);
+        e = tks::launch_append(a, s->dim, s->key_dtype == TKS_KEY_FP8_E4M3FN, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    return TKS_OK;
+}
+
 namespace {
 
 struct BlockPlan {
@@ -611,7 +658,8 @@ int tks_profile_enable(int on) {
 
 int tks_profile_read(const char* role, double* total_ms, int64_t* launches) {
     static const char* kRoles[] = {"score_flat",   "score_pooled",  "score_refine", "select_flat",
-                                   "select_pooled", "select_refine", "select_scores", "pool"};
+                                   "select_pooled", "select_refine", "select_scores", "pool",
+                                   "append"};
     if (!role || !total_ms || !launches) return fail(TKS_EINVAL, "NULL argument");
     bool known = false;
     for (const char* r : kRoles) known = known || strcmp(r, role) == 0;

@@ -75,6 +75,23 @@ struct PoolArgs {
     uint16_t* out;
 };
 
+// Key-cache append (append.hip): compressed keys g0 .. g1-1 of every
+// sequence are completed by this call; jobs are the blocks J0 .. J0+n_jobs-1
+// of `span` compressed keys (the pooled block size, or a job size when
+// pooled is null).
+struct AppendArgs {
+    const uint16_t* raw;  // bf16 [batch, n_new, D]
+    uint16_t* tail;       // bf16 [batch, m, D] staging (m > 1)
+    void* k;              // [batch, n_k, D] bf16 or e4m3fn codes
+    float* k_scale;       // [batch, n_k] (fp8)
+    uint16_t* pooled;     // bf16 [batch, n_k / span, D] or null
+    int32_t batch, n_k, n_new, m;
+    int32_t raw_len;
+    int32_t g0, g1;
+    int32_t span;
+    int32_t J0, n_jobs;
+};
+
 hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
                         hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream);
@@ -90,5 +107,6 @@ size_t select_split_workspace(int64_t n_rows, const SelectSplit& sp);
 hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const SelectSplit& sp,
                                void* ws, hipStream_t stream);
 hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int dim, bool fp8, hipStream_t stream);
 
 }  // namespace tks

@@ -51,8 +51,8 @@ class Shape:
 SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat_workspace",
            "tks_topk_flat", "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
-           "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_profile_enable",
-           "tks_profile_read")
+           "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_kv_append",
+           "tks_profile_enable", "tks_profile_read")
 
 _lib = None
 
@@ -85,10 +85,11 @@ def lib() -> ctypes.CDLL:
     L.tks_hisa_refine_workspace.argtypes = [SP, i32, i32, i32, i32]
     L.tks_hisa_refine_workspace.restype = sz
     L.tks_hisa_refine_topk.argtypes = [SP, P, P, P, P, i32, P, i32, i32, i32, P, P, P, sz, P]
+    L.tks_kv_append.argtypes = [SP, P, i32, i32, P, P, P, i32, P, P]
     L.tks_profile_enable.argtypes = [ctypes.c_int]
     L.tks_profile_read.argtypes = [ctypes.c_char_p, P, P]
     for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
-            L.tks_hisa_block_select, L.tks_hisa_refine_topk:
+            L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append:
         s.restype = ctypes.c_int
     _lib = L
     return L
@@ -213,6 +214,21 @@ def hisa_pool_keys(shape: Shape, k, k_scale, block, pooled=None):
     _check(lib().tks_hisa_pool_keys(ctypes.byref(S), _p(k), _p(k_scale), block, _p(pooled),
                                     _stream()))
     return pooled
+
+
+def kv_append(shape: Shape, raw, raw_len, k, k_scale=None, raw_tail=None, block=0, pooled=None):
+    """Append raw bf16 keys [batch, n_new, dim] to the compressed key cache
+    (k, k_scale) whose raw streams hold raw_len keys; with block > 0 the
+    completed pooled blocks are written to pooled [batch, n_k // block, dim].
+    raw_tail: bf16 [batch, causal_ratio, dim] staging kept between calls."""
+    _dev(raw, "raw", _BF16), _dev(k, "k", _key_dtypes(shape))
+    _dev(k_scale, "k_scale", (torch.float32,)), _dev(raw_tail, "raw_tail", _BF16)
+    _dev(pooled, "pooled", _BF16)
+    if raw.dim() != 3 or raw.shape[0] != shape.batch or raw.shape[2] != shape.dim:
+        raise ValueError("raw must be [batch, n_new, dim]")
+    S = shape.c()
+    _check(lib().tks_kv_append(ctypes.byref(S), _p(raw), raw.shape[1], int(raw_len), _p(raw_tail),
+                               _p(k), _p(k_scale), int(block), _p(pooled), _stream()))
 
 
 def m_total_of(m_scored: int, force_flags: int) -> int:
