@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk-standalone", action="store_true",
                     help="skip the selection-only measurement on a 1 GiB score matrix")
+    ap.add_argument("--no-kv-append", action="store_true",
+                    help="skip the key-cache append measurement (bulk build + decode appends)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -371,6 +373,13 @@ def main():
                   frac_hbm=round(tb / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
         del sc, t_idx, t_val, t_ws
 
+    # ---- key-cache append (compression + fp8 quantisation + pooled blocks in
+    # one pass): the workload's cache built from raw keys by one bulk append,
+    # then one pooled-block cycle of single-key decode appends
+    ka = None
+    if not args.no_kv_append:
+        ka = kv_append_bench(cfg, S, tks, dev, hisa, k, ks, ev, kern.get("pool"))
+
     line = {
         "metric": METRIC, "value": value, "unit": "q-k scores/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -384,8 +393,86 @@ def main():
         "kernels": kern,
         "hbm_bytes": mem,
         "topk_standalone": ts,
+        "kv_append": ka,
     }
     print(json.dumps(line), flush=True)
+
+
+def kv_append_bench(cfg, S, tks, dev, hisa, k, ks, ev, pool_role):
+    """Times tks_kv_append on the workload's cache shape with its own buffers:
+    a bulk build of the whole cache (raw keys read once, codes, scales and
+    pooled blocks written once) and a cycle of single-key appends that
+    completes one pooled block.  The cycle re-appends the last raw keys, so
+    the cache must come out identical to the bulk build."""
+    import torch
+    m = cfg.causal_ratio
+    B = cfg.block if hisa else 0
+    n_raw = cfg.n_k * m
+    g = torch.Generator(device=dev).manual_seed(777)
+    raw = torch.randn((cfg.batch, n_raw, cfg.dim), device=dev, generator=g).to(torch.bfloat16)
+    k_a = torch.empty_like(k)
+    ks_a = torch.empty_like(ks) if ks is not None else None
+    p_a = (torch.empty((cfg.batch, cfg.n_k // B, cfg.dim), dtype=torch.bfloat16, device=dev)
+           if B else None)
+    tail = torch.zeros((cfg.batch, m, cfg.dim), dtype=torch.bfloat16, device=dev) if m > 1 else None
+    sa = tks.Shape(cfg.batch, 1, cfg.n_k, 1, cfg.dim, causal_ratio=m, key_dtype=cfg.key_dtype)
+    app = lambda r, pos: tks.kv_append(sa, r, pos, k_a, ks_a, tail, B, p_a)
+
+    for _ in range(2):
+        app(raw, 0)
+    e0, e1 = ev(), ev()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        app(raw, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk_ms = e0.elapsed_time(e1) / reps
+    nbytes = raw.numel() * 2 + k_a.numel() * k_a.element_size() + \
+        (ks_a.numel() * 4 if ks_a is not None else 0) + (p_a.numel() * 2 if p_a is not None else 0)
+    ref_k = k_a.clone()
+    ref_p = p_a.clone() if p_a is not None else None
+
+    cyc = m * (B or 64)
+    r0 = n_raw - cyc
+    singles = [raw[:, p:p + 1].contiguous() for p in range(r0, n_raw)]
+    for i, r in enumerate(singles):
+        app(r, r0 + i)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for i, r in enumerate(singles):
+        app(r, r0 + i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / cyc
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i, r in enumerate(singles):
+            app(r, r0 + i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(3):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (3 * cyc)
+    same = bool(torch.equal(k_a, ref_k) and (p_a is None or torch.equal(p_a, ref_p)))
+    del graph
+    out = dict(
+        ratio=m, block=B, raw_keys_per_seq=n_raw,
+        bulk=dict(ms=round(bulk_ms, 4), bytes=int(nbytes),
+                  gb_per_s=round(nbytes / (bulk_ms * 1e-3) / 1e9, 1),
+                  frac_hbm=round(nbytes / (bulk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
+        decode=dict(appends=cyc, us_per_append_eager=round(eager_us, 2),
+                    us_per_append_graph=round(graph_us, 2),
+                    full_pool_us=round(pool_role["avg_ms"] * 1e3, 1) if pool_role else None),
+        cache_identical_to_bulk=same)
+    del raw, k_a, ks_a, p_a, tail, singles, ref_k, ref_p
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(cfg, k_np, ks_np, nvis, target_s):

@@ -125,13 +125,13 @@ def test_single_token_appends_cross_block_boundaries(m, fp8):
     c.check(raw, what="end")
 
 
-@pytest.mark.parametrize("fp8", [True, False])
-def test_special_values(fp8):
-    """All-zero keys (fp8 scale 0), -0, bf16 subnormals, the largest bf16
-    magnitudes and exact mean ties."""
-    batch, dim, m, block = 2, 64, 4, 32
+@pytest.mark.parametrize("fp8,m", [(True, 4), (False, 4), (True, 1), (False, 1)])
+def test_special_values(fp8, m):
+    """All-zero keys (fp8 scale 0), -0 (a mean is a sum from +0: it comes out
+    +0), bf16 subnormals, the largest bf16 magnitudes and exact mean ties."""
+    batch, dim, block = 2, 64, 32
     n_raw = m * block * 2
-    say("append special values fp8 %d" % fp8)
+    say("append special values fp8 %d m %d" % (fp8, m))
     raw = gen_raw_keys(5, batch, n_raw, dim)
     raw[0, 0:4] = 0                         # all-zero compressed key
     raw[0, 4:8] = 0x8000                    # -0

@@ -42,22 +42,17 @@ __device__ inline uint32_t f64_to_bf16(double x) {
     return u >> 16;
 }
 
-// OCP e4m3fn code of x: nearest magnitude, ties to the even code, saturated
-// at 448, sign bit kept.  Below 2^-6 the grid is the subnormal step 2^-9;
-// above, the 3-bit significand is rounded to nearest-even, and a carry out of
-// it moves to the next binade's first code by plain addition.
-__device__ inline uint32_t e4m3fn_code(float x) {
-    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-    const float a = fminf(fabsf(x), 448.0f);
-    uint32_t code;
-    if (a < 0.015625f) {
-        code = (uint32_t)rintf(a * 512.0f);
-    } else {
-        const uint32_t u = __float_as_uint(a);
-        const uint32_t mant = u & 0x7FFFFFu;
-        code = (((u >> 23) - 120u) << 3) + ((mant + 0x7FFFFu + ((mant >> 20) & 1u)) >> 20);
-    }
-    return sign | code;
+// OCP e4m3fn codes of four values (byte i = x[i]): nearest magnitude, ties
+// to the even code, sign kept, saturated at 448 -- the clamp keeps every
+// input inside the finite range, where v_cvt_pk_fp8_f32 rounds to nearest
+// even.
+__device__ inline uint32_t e4m3fn_x4(const float* x) {
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(x[i], -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+    return (uint32_t)w;
 }
 
 __device__ inline void add_bf16x8(double* acc, const u32x4& v) {
@@ -84,7 +79,7 @@ __device__ inline void add_fp8x8(double* acc, uint32_t c0, uint32_t c1, float sc
     }
 }
 
-template <bool FP8, int D>
+template <bool FP8, int D, bool M1>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     constexpr int TPG = D / 8;  // threads per key (8 dims each)
     const int64_t gt = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -93,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     if (job >= (int64_t)a.batch * a.n_jobs) return;
     const int32_t b = (int32_t)(job / a.n_jobs);
     const int32_t J = a.J0 + (int32_t)(job % a.n_jobs);
-    const int32_t m = a.m;
+    const int32_t m = M1 ? 1 : a.m;
     const int32_t gs = max(a.g0, J * a.span);          // groups completed here
     const int32_t ge = min(a.g1, (J + 1) * a.span);
     const bool pool = a.pooled != nullptr && (J + 1) * a.span <= a.g1;
@@ -135,9 +130,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         }
     }
 
-    // raw row at position p: staged (p < raw_len) or new
+    // raw row at position p: staged (p < raw_len, only in group g0, whose
+    // slot is p mod m = p - m * g0) or new
+    const int64_t tail0 = (int64_t)m * a.g0;
     auto raw_row = [&](int64_t p) -> const u32x4* {
-        const uint16_t* src = p < raw_len ? a.tail + ((int64_t)b * m + p % m) * D
+        const uint16_t* src = p < raw_len ? a.tail + ((int64_t)b * m + (p - tail0)) * D
                                           : a.raw + ((int64_t)b * a.n_new + (p - raw_len)) * D;
         return reinterpret_cast<const u32x4*>(src + 8 * piece);
     };
@@ -145,60 +142,113 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     double gsum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) gsum[e] = 0.0;
+    // the mean divides by m: for a power of two, multiplying by the exact
+    // reciprocal is the same operation (no fp64 underflow at bf16 magnitudes)
+    const bool m_pow2 = (m & (m - 1)) == 0;
+    const double inv_m = 1.0 / (double)m;
     const int64_t p_end = (int64_t)m * ge;
     int32_t r = 0;       // position within the current group
     int32_t g = gs;      // current group
-    for (int64_t p = (int64_t)m * gs; p < p_end; p += kAhead) {
-        u32x4 v[kAhead];
+    // one raw row of the job, in position order
+    auto consume = [&](const u32x4& row_in) {
+        // kw: the compressed key's 8 bf16 values, packed in pairs
+        u32x4 kw;
+        if constexpr (M1) {
+            // the mean of one bf16 key is that key, except that a sum
+            // starting from +0 turns -0 into +0
+            kw = row_in;
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u) v[u] = __builtin_nontemporal_load(raw_row(min(p + u, p_end - 1)));
-#pragma unroll
-        for (int u = 0; u < kAhead; ++u) {
-            if (p + u >= p_end) break;
-            add_bf16x8(gsum, v[u]);
-            if (++r < m) continue;
+            for (int w = 0; w < 4; ++w) {
+                uint32_t z = kw[w];
+                if ((z & 0x7FFFu) == 0) z &= ~0x8000u;
+                if ((z & 0x7FFF0000u) == 0) z &= ~0x80000000u;
+                kw[w] = z;
+            }
+        } else {
+            add_bf16x8(gsum, row_in);
+            if (++r < m) return;
             // group g complete: round the mean once to bf16
             uint32_t kc[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                kc[e] = f64_to_bf16(gsum[e] / (double)m);
+                kc[e] = f64_to_bf16(m_pow2 ? gsum[e] * inv_m : gsum[e] / (double)m);
                 gsum[e] = 0.0;
             }
-            const int64_t row = kbase + g;
-            if constexpr (FP8) {
-                float amax = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(__uint_as_float(kc[e] << 16)));
-#pragma unroll
-                for (int o = 1; o < TPG; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, TPG));
-                const float scale = amax / 448.0f;
-                const float div = scale > 0.0f ? scale : 1.0f;
-                uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    c0 |= e4m3fn_code(__uint_as_float(kc[e] << 16) / div) << (8 * e);
-                    c1 |= e4m3fn_code(__uint_as_float(kc[4 + e] << 16) / div) << (8 * e);
-                }
-                *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.k) + row * D + 8 * piece) = u32x2{c0, c1};
-                if (piece == 0) a.k_scale[row] = scale;
-                if (pool) add_fp8x8(pacc, c0, c1, scale);
-            } else {
-                const u32x4 o = u32x4{kc[0] | (kc[1] << 16), kc[2] | (kc[3] << 16),
-                                      kc[4] | (kc[5] << 16), kc[6] | (kc[7] << 16)};
-                *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k) + row * D + 8 * piece) = o;
-                if (pool) add_bf16x8(pacc, o);
-            }
+            kw = u32x4{kc[0] | (kc[1] << 16), kc[2] | (kc[3] << 16), kc[4] | (kc[5] << 16),
+                       kc[6] | (kc[7] << 16)};
             r = 0;
-            ++g;
         }
+        const int64_t row = kbase + g;
+        if constexpr (FP8) {
+            float x[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                x[2 * w] = __uint_as_float(kw[w] << 16);
+                x[2 * w + 1] = __uint_as_float(kw[w] & 0xFFFF0000u);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+            for (int o = 1; o < TPG; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, TPG));
+            const float scale = amax / 448.0f;
+            const float div = scale > 0.0f ? scale : 1.0f;
+            if (div >= 0x1p-60f) {
+                // x / div correctly rounded from the correctly rounded
+                // reciprocal y: two fma residual corrections bring the
+                // quotient within one ulp, and Markstein's theorem
+                // (y = RN(1/div), residual exact) makes the last one
+                // round correctly.  div >= 2^-60 keeps every residual
+                // that can change a code in the normal range; the sign
+                // is restored for -0.
+                const float y = 1.0f / div;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float q0 = x[e] * y;
+                    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, div, x[e]), y, q0);
+                    const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, div, x[e]), y, q1);
+                    x[e] = __builtin_copysignf(q2, x[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = x[e] / div;
+            }
+            const uint32_t c0 = e4m3fn_x4(x), c1 = e4m3fn_x4(x + 4);
+            *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.k) + row * D + 8 * piece) = u32x2{c0, c1};
+            if (piece == 0) a.k_scale[row] = scale;
+            if (pool) add_fp8x8(pacc, c0, c1, scale);
+        } else {
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k) + row * D + 8 * piece) = kw;
+            if (pool) add_bf16x8(pacc, kw);
+        }
+        ++g;
+    };
+    // two batches of kAhead raw rows: one is consumed while the next loads
+    const int64_t p0 = (int64_t)m * gs;
+    u32x4 va[kAhead], vb[kAhead];
+    auto load = [&](u32x4* v, int64_t p) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) v[u] = __builtin_nontemporal_load(raw_row(min(p + u, p_end - 1)));
+    };
+    auto take = [&](const u32x4* v, int64_t p) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u)
+            if (p + u < p_end) consume(v[u]);
+    };
+    if (p0 < p_end) load(va, p0);
+    for (int64_t p = p0; p < p_end; p += 2 * kAhead) {
+        if (p + kAhead < p_end) load(vb, p + kAhead);
+        take(va, p);
+        if (p + 2 * kAhead < p_end) load(va, p + 2 * kAhead);
+        if (p + kAhead < p_end) take(vb, p + kAhead);
     }
 
     if (pool) {
+        const double inv_span = 1.0 / (double)a.span;  // exact: the block size is a power of two
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            o[e] = f64_to_bf16(pacc[2 * e] / (double)a.span) |
-                   (f64_to_bf16(pacc[2 * e + 1] / (double)a.span) << 16);
+            o[e] = f64_to_bf16(pacc[2 * e] * inv_span) | (f64_to_bf16(pacc[2 * e + 1] * inv_span) << 16);
         const int64_t nb = a.n_k / a.span;
         *reinterpret_cast<u32x4*>(a.pooled + ((int64_t)b * nb + J) * D + 8 * piece) =
             u32x4{o[0], o[1], o[2], o[3]};
@@ -207,11 +257,13 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     // stage the raw keys of the group left open (first job of the sequence,
     // after its own reads of the staged keys above)
     if (m > 1 && J == a.J0) {
+        // the open group is g1: raw position p sits in slot p - m * g1
         const int64_t end = raw_len + a.n_new;
-        for (int64_t p = max(raw_len, (int64_t)m * a.g1); p < end; ++p) {
+        const int64_t open0 = (int64_t)m * a.g1;
+        for (int64_t p = max(raw_len, open0); p < end; ++p) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(
                 a.raw + ((int64_t)b * a.n_new + (p - raw_len)) * D + 8 * piece);
-            *reinterpret_cast<u32x4*>(a.tail + ((int64_t)b * m + p % m) * D + 8 * piece) = v;
+            *reinterpret_cast<u32x4*>(a.tail + ((int64_t)b * m + (p - open0)) * D + 8 * piece) = v;
         }
     }
 }
@@ -221,7 +273,10 @@ void launch_d(const AppendArgs& a, hipStream_t stream) {
     constexpr int TPG = D / 8;
     const int64_t threads = (int64_t)a.batch * a.n_jobs * TPG;
     const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL((append_kernel<FP8, D>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.m == 1)
+        hipLaunchKernelGGL((append_kernel<FP8, D, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((append_kernel<FP8, D, false>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
 template <bool FP8>
