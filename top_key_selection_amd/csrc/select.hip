@@ -1066,7 +1066,6 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
 template <bool VEC, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows) {
     __shared__ SelectLds L;
-    const int tid = threadIdx.x;
     if ((int64_t)blockIdx.x >= n_rows) return;
     RowCtx r;
     int32_t count;
