@@ -474,6 +474,130 @@ __device__ __forceinline__ void sort_desc(uint64_t* u, uint64_t* tmp, int32_t n)
     }
 }
 
+// Sort the selected list L.u[0, n) descending, n <= kMaxK, by counting on
+// the score: the score range [vmin, vmax] of the list is cut into 4096
+// equal bins (fp32 (v - vmin) * scale, a non-decreasing map of the score),
+// each entry is scattered to its bin's run (bins in descending order,
+// positions from an exclusive scan of the bin counts), and inside a bin its
+// final place is the number of bin entries above it in the total order
+// (independent LDS reads, no dependency chain).  Scores spread the entries
+// over many bins, a few per bin; a bin of more than kBinCap entries (heavy
+// ties, clustered scores) or a non-finite range takes the bitonic / merge
+// sort instead.  The 4096 counters and the scattered copy use the candidate
+// area after the selected list.
+constexpr int kSortBins = 4096;
+constexpr int kBinCap = 128;
+static_assert(kMaxK * 8 + kSortBins * 4 <= kCap * 8, "bin sort scratch fits the candidate area");
+
+template <int NT>
+__device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
+    constexpr int W = NT / kWave;
+    constexpr int EPT = (kMaxK + NT - 1) / NT;
+    constexpr int per = kSortBins / NT;  // bins per thread in the scan, descending
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t* u = L.u;
+    uint64_t* tmp = &L.u[kMaxK];
+    uint32_t* bins = reinterpret_cast<uint32_t*>(&L.u[kMaxK + kMaxK]);
+    if (n <= 1) return;
+    uint64_t e[EPT];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int j = tid + i * NT;
+        e[i] = j < n ? u[j] : 0;
+        if (j < n) {
+            kmin = min(kmin, (uint32_t)(e[i] >> 32));
+            kmax = max(kmax, (uint32_t)(e[i] >> 32));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if (lane == 0) {
+        L.hist8[wave] = kmin;
+        L.hist8[64 + wave] = kmax;
+    }
+    for (int i = tid; i < kSortBins; i += NT) bins[i] = 0u;
+    __syncthreads();
+    kmin = L.hist8[0];
+    kmax = L.hist8[64];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+        kmin = min(kmin, L.hist8[w]);
+        kmax = max(kmax, L.hist8[64 + w]);
+    }
+    const float vmin = key_score(kmin), vspan = key_score(kmax) - vmin;
+    if (!(vspan < __builtin_inff())) {  // a non-finite score or range
+        sort_desc<NT>(u, tmp, n);
+        return;
+    }
+    const float scale = vspan > 0.0f ? (float)(kSortBins - 1) / vspan : 0.0f;
+    uint32_t bin[EPT], rank[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const float v = key_score((uint32_t)(e[i] >> 32));
+        bin[i] = min((uint32_t)((v - vmin) * scale), (uint32_t)(kSortBins - 1));
+        rank[i] = tid + i * NT < n ? atomicAdd(&bins[bin[i]], 1u) : 0u;
+    }
+    __syncthreads();
+    // run starts: bins in descending order, exclusive scan of the counts
+    uint32_t c[per];
+    int32_t sum = 0;
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = bins[kSortBins - 1 - (per * tid + i)];
+        sum += (int32_t)c[i];
+        mx = max(mx, c[i]);
+    }
+    int32_t inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if (lane == 63) L.wsum[wave] = inc;
+    if (lane == 0) L.hist8[128 + wave] = mx;
+    __syncthreads();
+    int32_t run = inc - sum;
+    uint32_t maxc = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        run += w < wave ? L.wsum[w] : 0;
+        maxc = max(maxc, L.hist8[128 + w]);
+    }
+    if (maxc > (uint32_t)kBinCap) {
+        // u is untouched: the general sort takes over (its first writes
+        // go past n, and tmp is read by nobody any more)
+        sort_desc<NT>(u, tmp, n);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        bins[kSortBins - 1 - (per * tid + i)] = (uint32_t)run;
+        run += (int32_t)c[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+        if (tid + i * NT < n) tmp[bins[bin[i]] + rank[i]] = e[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        if (tid + i * NT >= n) continue;
+        const uint32_t st = bins[bin[i]];
+        const uint32_t end = bin[i] == 0 ? (uint32_t)n : bins[bin[i] - 1];
+        uint32_t r = 0;
+        for (uint32_t t = st; t < end; ++t) r += tmp[t] > e[i] ? 1u : 0u;
+        u[st + r] = e[i];
+    }
+    __syncthreads();
+}
+
 // Write a finished row: sel[0, n_sel) sorted descending on the composite.
 template <int NT>
 __device__ __forceinline__ void write_row(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t n_sel,
@@ -1077,7 +1201,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     __syncthreads();
     // (block-select output is ordered by block index: write_row does that;
     // the running list of a non-final tile needs no order)
-    if (!a.blockselect && final_out) sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
+    if (!a.blockselect && final_out) sort_final<NT>(L, n_sel);
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
@@ -1188,7 +1312,7 @@ __global__ __launch_bounds__(NT) void prefilter_finish_kernel(SelectArgs a, int6
         n_sel = select_hist<VEC, NT>(a, r, L, K);
     }
     __syncthreads();
-    sort_desc<NT>(L.u, &L.u[kMaxK], n_sel);
+    sort_final<NT>(L, n_sel);
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
