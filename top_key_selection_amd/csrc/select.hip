@@ -1145,13 +1145,31 @@ __device__ __forceinline__ int32_t resolve_pool(SelectLds& L, int32_t n_pool, in
 // answer; they are found by an LDS radix select.  A pool that is too small
 // or overflows falls back to the full histogram path.
 template <bool VEC, int NT>
-__device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
+__device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K,
+                                               bool& sorted) {
     const int tid = threadIdx.x;
+    sorted = false;
     if (K <= 0) return 0;
     const int32_t n_cols = max(0, r.hi - r.lo);
     const int32_t n_total = n_cols + (r.prior ? prior_len(a) : 0);
     uint64_t* cand = &L.u[kMaxK];
     uint32_t tau = 0;
+    if (n_total > K && n_total <= kMaxK) {
+        // few candidates: gather them all and sort them; the best K lead
+        if (tid == 0) L.cnt[1] = 0;
+        __syncthreads();
+        auto c = [&](bool valid, uint32_t key, int32_t idx) {
+            const int32_t pos = wave_append(&L.cnt[1], valid);
+            if (valid) L.u[pos] = composite(key, idx);
+        };
+        visit_prior<NT>(a, r, c);
+        collect_ge<VEC, NT>(a, r, r.lo, r.hi, 0u, &L.cnt[1], L.u, kMaxK);
+        __syncthreads();
+        const int32_t n = L.cnt[1];
+        sort_final<NT>(L, n);
+        sorted = true;
+        return min(K, n);
+    }
     if (n_total > K && n_total < kPrefilterMin) return select_hist<VEC, NT>(a, r, L, K);
     if (n_total > kCap) {
         const int32_t target = K + K / 2 - K / 10 + 32;
@@ -1197,11 +1215,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a, int64_t n_rows
     if (!a.always_final && a.tile_begin > 0 && count <= a.tile_begin) return;
     const bool final_out = a.always_final || count <= a.tile_end;
     const int32_t K = a.topk;
-    const int32_t n_sel = select_core<VEC, NT>(a, r, L, K);
+    bool sorted;
+    const int32_t n_sel = select_core<VEC, NT>(a, r, L, K, sorted);
     __syncthreads();
     // (block-select output is ordered by block index: write_row does that;
     // the running list of a non-final tile needs no order)
-    if (!a.blockselect && final_out) sort_final<NT>(L, n_sel);
+    if (!a.blockselect && final_out && !sorted) sort_final<NT>(L, n_sel);
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
