@@ -474,37 +474,34 @@ __device__ __forceinline__ void sort_desc(uint64_t* u, uint64_t* tmp, int32_t n)
     }
 }
 
-// Sort the selected list L.u[0, n) descending, n <= kMaxK, by counting on
-// the score: the score range [vmin, vmax] of the list is cut into 4096
-// equal bins (fp32 (v - vmin) * scale, a non-decreasing map of the score),
-// each entry is scattered to its bin's run (bins in descending order,
-// positions from an exclusive scan of the bin counts), and inside a bin its
-// final place is the number of bin entries above it in the total order
-// (independent LDS reads, no dependency chain).  Scores spread the entries
-// over many bins, a few per bin; a bin of more than kBinCap entries (heavy
-// ties, clustered scores) or a non-finite range takes the bitonic / merge
-// sort instead.  The 4096 counters and the scattered copy use the candidate
-// area after the selected list.
+// The best K of src[0, n) (distinct composites), sorted descending, into
+// out[0, min(K, n)), by counting on the score: the score range [vmin, vmax]
+// is cut into 4096 equal bins (fp32 (v - vmin) * scale, a non-decreasing
+// map of the score), each entry is scattered to its bin's run (bins in
+// descending order, run starts from an exclusive scan of the bin counts),
+// and inside a bin its place is the number of bin entries above it in the
+// total order (independent LDS reads, no dependency chain); entries placed
+// at K or beyond are dropped.  Scores spread the entries over many bins, a
+// few per bin.  Every entry is first taken into registers, so tmp may alias
+// src and bins may alias out.  Returns false with src untouched when
+// counting does not apply: a non-finite score range, or a bin of more than
+// kBinCap entries (heavy ties, clustered scores).
 constexpr int kSortBins = 4096;
 constexpr int kBinCap = 128;
-static_assert(kMaxK * 8 + kSortBins * 4 <= kCap * 8, "bin sort scratch fits the candidate area");
 
-template <int NT>
-__device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
+template <int NT, int NMAX>
+__device__ __forceinline__ bool counting_topk(SelectLds& L, const uint64_t* src, int32_t n, int32_t K,
+                                              uint64_t* out, uint64_t* tmp, uint32_t* bins) {
     constexpr int W = NT / kWave;
-    constexpr int EPT = (kMaxK + NT - 1) / NT;
+    constexpr int EPT = (NMAX + NT - 1) / NT;
     constexpr int per = kSortBins / NT;  // bins per thread in the scan, descending
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint64_t* u = L.u;
-    uint64_t* tmp = &L.u[kMaxK];
-    uint32_t* bins = reinterpret_cast<uint32_t*>(&L.u[kMaxK + kMaxK]);
-    if (n <= 1) return;
     uint64_t e[EPT];
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int j = tid + i * NT;
-        e[i] = j < n ? u[j] : 0;
+        e[i] = j < n ? src[j] : 0;
         if (j < n) {
             kmin = min(kmin, (uint32_t)(e[i] >> 32));
             kmax = max(kmax, (uint32_t)(e[i] >> 32));
@@ -530,8 +527,8 @@ __device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
     }
     const float vmin = key_score(kmin), vspan = key_score(kmax) - vmin;
     if (!(vspan < __builtin_inff())) {  // a non-finite score or range
-        sort_desc<NT>(u, tmp, n);
-        return;
+        __syncthreads();
+        return false;
     }
     const float scale = vspan > 0.0f ? (float)(kSortBins - 1) / vspan : 0.0f;
     uint32_t bin[EPT], rank[EPT];
@@ -571,10 +568,8 @@ __device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
         maxc = max(maxc, L.hist8[128 + w]);
     }
     if (maxc > (uint32_t)kBinCap) {
-        // u is untouched: the general sort takes over (its first writes
-        // go past n, and tmp is read by nobody any more)
-        sort_desc<NT>(u, tmp, n);
-        return;
+        __syncthreads();
+        return false;
     }
 #pragma unroll
     for (int i = 0; i < per; ++i) {
@@ -582,20 +577,39 @@ __device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
         run += (int32_t)c[i];
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-        if (tid + i * NT < n) tmp[bins[bin[i]] + rank[i]] = e[i];
-    __syncthreads();
+    // scatter; bin[] now holds the run start, rank[] the run end
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         if (tid + i * NT >= n) continue;
         const uint32_t st = bins[bin[i]];
-        const uint32_t end = bin[i] == 0 ? (uint32_t)n : bins[bin[i] - 1];
-        uint32_t r = 0;
-        for (uint32_t t = st; t < end; ++t) r += tmp[t] > e[i] ? 1u : 0u;
-        u[st + r] = e[i];
+        const uint32_t en = bin[i] == 0 ? (uint32_t)n : bins[bin[i] - 1];
+        tmp[st + rank[i]] = e[i];
+        bin[i] = st;
+        rank[i] = en;
     }
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        if (tid + i * NT >= n || bin[i] >= (uint32_t)K) continue;
+        uint32_t r = 0;
+        for (uint32_t t = bin[i]; t < rank[i]; ++t) r += tmp[t] > e[i] ? 1u : 0u;
+        if (bin[i] + r < (uint32_t)K) out[bin[i] + r] = e[i];
+    }
+    __syncthreads();
+    return true;
+}
+
+// Sort the selected list L.u[0, n) descending, n <= kMaxK: counting (the
+// scattered copy and the 4096 counters use the candidate area after the
+// list), else the bitonic / merge sort.
+static_assert(kMaxK * 8 + kSortBins * 4 <= kCap * 8, "counting scratch fits the candidate area");
+
+template <int NT>
+__device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
+    if (n <= 1) return;
+    if (!counting_topk<NT, kMaxK>(L, L.u, n, n, L.u, &L.u[kMaxK],
+                                  reinterpret_cast<uint32_t*>(&L.u[kMaxK + kMaxK])))
+        sort_desc<NT>(L.u, &L.u[kMaxK], n);
 }
 
 // Write a finished row: sel[0, n_sel) sorted descending on the composite.
@@ -991,8 +1005,10 @@ __device__ __forceinline__ void setup_row(const SelectArgs& a, RowCtx& r, Select
 // Exact selection by a full histogram of the row (the path that never
 // fails): the row's top-K candidates into L.u[0, n) (unsorted); returns n.
 template <bool VEC, int NT>
-__device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K) {
+__device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx& r, SelectLds& L, int32_t K,
+                                               bool& sorted) {
     const int tid = threadIdx.x;
+    sorted = false;
     if (K <= 0) return 0;
     uint32_t* hist = lds_hist(L);
     // pass 1: 12-bit histogram
@@ -1007,8 +1023,23 @@ __device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx
     const int32_t above = L.pick[1], inbin = L.pick[2], total = L.pick[3];
     __syncthreads();
     if (bstar >= 0 && inbin > kCap && inbin != K - above) return radix_fallback<VEC, NT>(a, r, L, K);
-    // pass 2: collect
     const bool all = bstar < 0;  // total <= K
+    if (!all && above + inbin <= kCap) {
+        // pass 2: everything from the threshold bin up into the pool, whose
+        // best K are then placed in order
+        if (tid == 0) L.cnt[1] = 0;
+        __syncthreads();
+        auto cp = [&](bool valid, uint32_t key, int32_t idx) {
+            const bool p = valid && (int32_t)(key >> kBinShift) >= bstar;
+            const int32_t pos = wave_append(&L.cnt[1], p);
+            if (p) L.u[kMaxK + pos] = composite(key, idx);
+        };
+        visit_prior<NT>(a, r, cp);
+        visit_columns<VEC, NT>(a, r, r.lo, r.hi, cp);
+        __syncthreads();
+        return pool_best<NT>(L, above + inbin, K, sorted);
+    }
+    // pass 2: collect
     const bool whole_bin = !all && inbin == K - above;
     if (tid == 0) {
         L.cnt[0] = 0;
@@ -1132,6 +1163,16 @@ __device__ __forceinline__ int32_t resolve_pool(SelectLds& L, int32_t n_pool, in
                                       0xFFFull << 52, inbin);
 }
 
+// The best K of the pool L.u[kMaxK, kMaxK + n) (K <= n <= kCap) into
+// L.u[0, K): sorted by counting when it applies (sorted = true), else by
+// the radix select (unsorted).  Returns K.
+template <int NT>
+__device__ __forceinline__ int32_t pool_best(SelectLds& L, int32_t n_pool, int32_t K, bool& sorted) {
+    uint64_t* cand = &L.u[kMaxK];
+    sorted = counting_topk<NT, kCap>(L, cand, n_pool, K, L.u, cand, reinterpret_cast<uint32_t*>(L.u));
+    return sorted ? K : resolve_pool<NT>(L, n_pool, K);
+}
+
 // Exact selection of the row's top-K candidates into L.u[0, n) (unsorted);
 // returns n.
 //
@@ -1170,10 +1211,10 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
         sorted = true;
         return min(K, n);
     }
-    if (n_total > K && n_total < kPrefilterMin) return select_hist<VEC, NT>(a, r, L, K);
+    if (n_total > K && n_total < kPrefilterMin) return select_hist<VEC, NT>(a, r, L, K, sorted);
     if (n_total > kCap) {
         const int32_t target = K + K / 2 - K / 10 + 32;
-        if (!sample_threshold<NT>(a, r, L, n_total, target, tau)) return select_hist<VEC, NT>(a, r, L, K);
+        if (!sample_threshold<NT>(a, r, L, n_total, target, tau)) return select_hist<VEC, NT>(a, r, L, K, sorted);
     }
     // one pass: the pool of candidates with key >= tau (all of them when
     // tau = 0); a row that fits the answer goes straight to the list
@@ -1200,9 +1241,9 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
     }
     if (n_pool < K || n_pool > kCap) {
         __syncthreads();
-        return select_hist<VEC, NT>(a, r, L, K);
+        return select_hist<VEC, NT>(a, r, L, K, sorted);
     }
-    return resolve_pool<NT>(L, n_pool, K);
+    return pool_best<NT>(L, n_pool, K, sorted);
 }
 
 template <bool VEC, int NT>
@@ -1321,17 +1362,18 @@ __global__ __launch_bounds__(NT) void prefilter_finish_kernel(SelectArgs a, int6
     const uint32_t tau = w.tau[r.y];
     const int32_t n_pool = w.count[r.y];
     int32_t n_sel;
+    bool sorted = false;
     if (tau != kNoTau && ((tau == 0u && n_pool <= K) || (n_pool >= K && n_pool <= kCap))) {
         const uint64_t* src = w.pool + r.y * kCap;
         uint64_t* dst = n_pool <= K ? L.u : &L.u[kMaxK];
         for (int i = tid; i < n_pool; i += NT) dst[i] = src[i];
         __syncthreads();
-        n_sel = n_pool <= K ? n_pool : resolve_pool<NT>(L, n_pool, K);
+        n_sel = n_pool <= K ? n_pool : pool_best<NT>(L, n_pool, K, sorted);
     } else {
-        n_sel = select_hist<VEC, NT>(a, r, L, K);
+        n_sel = select_hist<VEC, NT>(a, r, L, K, sorted);
     }
     __syncthreads();
-    sort_final<NT>(L, n_sel);
+    if (!sorted) sort_final<NT>(L, n_sel);
     write_row<NT>(a, r, L, n_sel, final_out);
 }
 
