@@ -40,6 +40,7 @@ constexpr int kCap = 4096;          // LDS candidate list (entries of the thresh
 constexpr int kBins = 4096;         // 12-bit first digit
 constexpr int kBinShift = 20;
 constexpr int kSamples = 2048;      // candidates sampled for the prefilter threshold
+constexpr int kSampleRun = 16;      // ... in evenly spaced runs of consecutive candidates
 static_assert(kSamples % 256 == 0 && kSamples % 1024 == 0, "whole samples per thread");
 constexpr int kPrefilterMin = 16384; // rows at least this long take the prefilter
 constexpr int kMaxBlkEntries = 512;
@@ -1065,7 +1066,8 @@ __device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx
 }
 
 // Key threshold that about `target` of the row's n candidates (prior list,
-// then columns) reach, estimated from kSamples evenly spaced candidates:
+// then columns) reach, estimated from kSamples candidates (evenly spaced
+// runs of kSampleRun consecutive ones):
 // the key of the sample of rank target * valid_samples / n, resolved to 20
 // bits with two 12-bit LDS histograms.  n > kSamples.  Returns false when
 // the sample cannot place it.
@@ -1086,7 +1088,11 @@ __device__ __forceinline__ bool sample_threshold(const SelectArgs& a, const RowC
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int s = tid + i * NT;
-        const int32_t q = (int32_t)(((int64_t)s * n) / kSamples);
+        // run s / kSampleRun starts at an even spacing; a run covers 64
+        // consecutive bytes, so the sample touches 1/8 of the row's lines
+        // (single spaced samples would touch every line of a long row)
+        const int32_t q = min(n - 1, (int32_t)(((int64_t)(s / kSampleRun) * n) / (kSamples / kSampleRun)) +
+                                         s % kSampleRun);
         if (q < np) {
             v[i] = a.prior_idx[r.y * np + q] >= 0;
             x[i] = a.prior_val[r.y * np + q];
