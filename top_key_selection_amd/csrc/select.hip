@@ -269,16 +269,17 @@ __device__ __forceinline__ int32_t wave_append(int32_t* counter, bool pred) {
 
 // Threshold of the k best from a histogram (bins in LDS or global memory,
 // read through `get`): pick = {b*, count above b*, count in b*, total}.
-template <int NT, class G>
-__device__ __forceinline__ void find_threshold(G&& get, int32_t K, int32_t* pick, int32_t* wsum) {
+template <int NT, int NB, class G>
+__device__ __forceinline__ void find_threshold_n(G&& get, int32_t K, int32_t* pick, int32_t* wsum) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int kWaves = NT / kWave;
-    constexpr int per = kBins / NT;  // bins per thread, descending order
+    constexpr int per = NB >= NT ? NB / NT : 1;  // bins per thread, descending order
+    const bool has = NB >= NT || tid < NB;
     int32_t c[per];
     int32_t s = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
-        c[i] = (int32_t)get(kBins - 1 - (per * tid + i));
+        c[i] = has ? (int32_t)get(NB - 1 - (per * tid + i)) : 0;
         s += c[i];
     }
     int32_t inc = s;
@@ -307,7 +308,7 @@ __device__ __forceinline__ void find_threshold(G&& get, int32_t K, int32_t* pick
 #pragma unroll
         for (int i = 0; i < per; ++i) {
             if (cum < K && K <= cum + c[i]) {
-                pick[0] = kBins - 1 - (per * tid + i);
+                pick[0] = NB - 1 - (per * tid + i);
                 pick[1] = cum;
                 pick[2] = c[i];
             }
@@ -315,6 +316,11 @@ __device__ __forceinline__ void find_threshold(G&& get, int32_t K, int32_t* pick
         }
     }
     __syncthreads();
+}
+
+template <int NT, class G>
+__device__ __forceinline__ void find_threshold(G&& get, int32_t K, int32_t* pick, int32_t* wsum) {
+    find_threshold_n<NT, kBins>(static_cast<G&&>(get), K, pick, wsum);
 }
 
 // Value of lane ^ S, exchanged by the vector ALU (DPP quad permutes and row
@@ -1065,20 +1071,23 @@ __device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx
     return finish_from_candidates<NT>(L, above, inbin, K - above, 44);
 }
 
-// Key threshold that about `target` of the row's n candidates (prior list,
-// then columns) reach, estimated from kSamples candidates (evenly spaced
-// runs of kSampleRun consecutive ones):
-// the key of the sample of rank target * valid_samples / n, resolved to 20
-// bits with two 12-bit LDS histograms.  n > kSamples.  Returns false when
-// the sample cannot place it.
+// Key threshold that at least K of the row's n candidates (prior list, then
+// columns) reach with high probability, estimated from kSamples candidates
+// (evenly spaced runs of kSampleRun consecutive ones).  With sv valid
+// samples, the expected sample rank of the K-th best candidate is
+// m = K * sv / n; the threshold is the key of sample rank m + d, with a
+// margin d of three standard deviations of that rank (sqrt(m)) plus 4,
+// capped so that the expected pool stays within 90 % of kCap.  The key is
+// resolved to 16 bits with two 256-bin LDS histograms.  n > kSamples.
+// Returns false when the sample cannot place it.
 template <int NT>
 __device__ __forceinline__ bool sample_threshold(const SelectArgs& a, const RowCtx& r, SelectLds& L,
-                                                 int32_t n, int32_t target, uint32_t& tau) {
+                                                 int32_t n, int32_t K, uint32_t& tau) {
     const int tid = threadIdx.x;
     const int32_t np = r.prior ? prior_len(a) : 0;
     uint32_t* keys = reinterpret_cast<uint32_t*>(&L.u[kMaxK]);  // kSamples keys (0: no candidate)
-    uint32_t* hist = reinterpret_cast<uint32_t*>(L.u);          // kBins bins
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    uint32_t* hist = L.hist8;                                   // 256 bins
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
     if (tid == 0) L.cnt[0] = 0;
     __syncthreads();
     // every sample load is issued before any is used
@@ -1106,28 +1115,31 @@ __device__ __forceinline__ bool sample_threshold(const SelectArgs& a, const RowC
     for (int i = 0; i < PER; ++i) {
         const uint32_t key = v[i] ? score_key(x[i]) : 0u;
         keys[tid + i * NT] = key;
-        hist_add(hist, v[i], key >> kBinShift);
+        hist_add(hist, v[i], key >> 24);
         const uint64_t m = __ballot(v[i]);
         if ((threadIdx.x & 63) == 0 && m) atomicAdd(&L.cnt[0], (int32_t)__popcll(m));
     }
     __syncthreads();
     const int32_t sv = L.cnt[0];
-    const int64_t rs = ((int64_t)target * sv + n - 1) / n;
-    if (rs < 1 || rs >= sv) return false;
-    find_threshold<NT>([&](int b) { return hist[b]; }, (int32_t)rs, L.pick, L.wsum);
+    const float m = (float)K * (float)sv / (float)n;
+    const float dmax = (0.9f * kCap - (float)K) * (float)sv / (float)n;
+    const float rsf = ceilf(m + fminf(3.0f * sqrtf(m) + 4.0f, dmax));
+    if (!(rsf >= 1.0f) || rsf >= (float)sv) return false;
+    const int32_t rs = (int32_t)rsf;
+    find_threshold_n<NT, 256>([&](int b) { return hist[b]; }, rs, L.pick, L.wsum);
     const int32_t b1 = L.pick[0];
-    const int32_t r2 = (int32_t)rs - L.pick[1];
+    const int32_t r2 = rs - L.pick[1];
     __syncthreads();
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
     for (int s = tid; s < kSamples; s += NT) {
         const uint32_t k = keys[s];
-        hist_add(hist, k != 0u && (int32_t)(k >> kBinShift) == b1, (k >> 8) & (kBins - 1));
+        hist_add(hist, k != 0u && (int32_t)(k >> 24) == b1, (k >> 16) & 255u);
     }
     __syncthreads();
-    find_threshold<NT>([&](int b) { return hist[b]; }, r2, L.pick, L.wsum);
+    find_threshold_n<NT, 256>([&](int b) { return hist[b]; }, r2, L.pick, L.wsum);
     const int32_t b2 = L.pick[0];
-    tau = ((uint32_t)b1 << kBinShift) | (b2 >= 0 ? (uint32_t)b2 << 8 : 0u);
+    tau = ((uint32_t)b1 << 24) | (b2 >= 0 ? (uint32_t)b2 << 16 : 0u);
     __syncthreads();
     return true;
 }
@@ -1219,8 +1231,7 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
     }
     if (n_total > K && n_total < kPrefilterMin) return select_hist<VEC, NT>(a, r, L, K, sorted);
     if (n_total > kCap) {
-        const int32_t target = K + K / 2 - K / 10 + 32;
-        if (!sample_threshold<NT>(a, r, L, n_total, target, tau)) return select_hist<VEC, NT>(a, r, L, K, sorted);
+        if (!sample_threshold<NT>(a, r, L, n_total, K, tau)) return select_hist<VEC, NT>(a, r, L, K, sorted);
     }
     // one pass: the pool of candidates with key >= tau (all of them when
     // tau = 0); a row that fits the answer goes straight to the list
@@ -1312,7 +1323,7 @@ __global__ __launch_bounds__(NT) void prefilter_sample_kernel(SelectArgs a, int6
     uint32_t tau = 0;  // a row that fits the pool keeps every candidate
     if (n > kCap) {
         const int32_t K = a.topk;
-        if (!sample_threshold<NT>(a, r, L, n, K + K / 2 - K / 10 + 32, tau)) tau = kNoTau;
+        if (!sample_threshold<NT>(a, r, L, n, K, tau)) tau = kNoTau;
     }
     if (threadIdx.x == 0) {
         w.tau[r.y] = tau;
