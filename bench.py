@@ -49,6 +49,8 @@ def parse():
                     help="skip the selection-only measurement on a 1 GiB score matrix")
     ap.add_argument("--no-kv-append", action="store_true",
                     help="skip the key-cache append measurement (bulk build + decode appends)")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip the re-layout measurement of the selected latent KV rows")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -380,6 +382,13 @@ def main():
     if not args.no_kv_append:
         ka = kv_append_bench(cfg, S, tks, dev, hisa, k, ks, ev, kern.get("pool"))
 
+    # ---- re-layout of the rows the flat top-k selected: a synthetic 576-dim
+    # bf16 latent KV cache (512 + 64, the MLA latent of DeepSeek-V3.2-style
+    # sparse attention; the pages give no attention shapes), one row per key
+    ga = None
+    if not args.no_gather:
+        ga = gather_bench(cfg, tks, dev, f_idx, ev)
+
     line = {
         "metric": METRIC, "value": value, "unit": "q-k scores/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -394,6 +403,7 @@ def main():
         "hbm_bytes": mem,
         "topk_standalone": ts,
         "kv_append": ka,
+        "gather_selected": ga,
     }
     print(json.dumps(line), flush=True)
 
@@ -473,6 +483,33 @@ def kv_append_bench(cfg, S, tks, dev, hisa, k, ks, ev, pool_role):
     del raw, k_a, ks_a, p_a, tail, singles, ref_k, ref_p
     torch.cuda.empty_cache()
     return out
+
+
+def gather_bench(cfg, tks, dev, idx, ev, latent_dim=576):
+    """tks_gather_selected of the step's flat top-k indices over a latent KV
+    cache of the workload's shape: bytes = selected rows read + written once,
+    plus the indices."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(99)
+    kv = torch.randint(-32768, 32767, (cfg.batch, cfg.n_k, latent_dim), dtype=torch.int16, device=dev,
+                       generator=g)
+    out = torch.empty((cfg.batch, cfg.n_q, cfg.topk, latent_dim), dtype=torch.int16, device=dev)
+    for _ in range(2):
+        tks.gather_selected(kv, idx, out)
+    e0, e1 = ev(), ev()
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        tks.gather_selected(kv, idx, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * out.numel() * 2 + idx.numel() * 4
+    del kv, out
+    torch.cuda.empty_cache()
+    return dict(rows=int(idx.numel()), row_bytes=latent_dim * 2, ms=round(ms, 4), bytes=int(nbytes),
+                gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
 
 def cpu_baseline(cfg, k_np, ks_np, nvis, target_s):

@@ -211,6 +211,23 @@ int tks_hisa_refine_topk(const tks_shape* shape, const void* q, const float* w, 
                          hipStream_t stream);
 
 /*
+ * Re-layout of the selected rows for the sparse attention that consumes the
+ * indices (LongCat Sparse Attention abstract, strategy (1): scattered KV
+ * entries are copied into a contiguous, hardware-aligned layout so the
+ * consumer reads them with coalesced loads).
+ *   kv:  [batch, n_kv, row_bytes] bytes (any row type: bf16 latent KV, keys);
+ *   idx: int32 [batch, n_q, topk] (as tks_topk_flat / tks_hisa_refine_topk
+ *        write them; -1 = empty slot);
+ *   out: [batch, n_q, topk, row_bytes]; out[b, t, j] = kv[b, idx[b, t, j]],
+ *        zeros where idx is -1 or outside [0, n_kv).
+ * row_bytes must be a positive multiple of 16 (at most 65536); kv and out
+ * 16-byte aligned.  The slot order of idx is kept.
+ */
+int tks_gather_selected(const void* kv, int32_t batch, int32_t n_kv, int32_t row_bytes,
+                        const int32_t* idx, int32_t n_q, int32_t topk, void* out,
+                        hipStream_t stream);
+
+/*
  * Kernel timing instrumentation (for benchmarks and profiling).  While
  * enabled, every kernel launch the library makes is bracketed by a pair of
  * HIP events recorded on the launch's stream.  tks_profile_enable(1) clears
@@ -225,6 +242,7 @@ int tks_hisa_refine_topk(const tks_shape* shape, const void* q, const float* w, 
  *   "select_scores" -- tks_topk_scores
  *   "pool"          -- tks_hisa_pool_keys
  *   "append"        -- tks_kv_append
+ *   "gather"        -- tks_gather_selected
  * Returns TKS_EINVAL for an unknown role or NULL outputs.
  */
 int tks_profile_enable(int on);

@@ -230,3 +230,21 @@ def compress_keys(raw, ratio: int, key_fp8: bool, n_k: int | None = None):
     _check(lib().orc_compress_keys(ctypes.byref(S), _ptr(raw), n_raw, _ptr(k), _ptr(ks)),
            "compress_keys")
     return k, ks
+
+
+def gather_selected(kv, idx):
+    """Re-layout of the selected rows (LongCat Sparse Attention abstract,
+    strategy (1): scattered KV entries copied into a contiguous layout):
+    out[b, t, j] = kv[b, idx[b, t, j]] when 0 <= idx < n_kv, zeros otherwise.
+    kv: [batch, n_kv, ...] numpy array; idx: int [batch, n_q, topk].  Plain
+    loops over (b, t, j): for small inputs and sampled rows."""
+    kv = np.asarray(kv)
+    idx = np.asarray(idx)
+    out = np.zeros(idx.shape + kv.shape[2:], kv.dtype)
+    for b in range(idx.shape[0]):
+        for t in range(idx.shape[1]):
+            for j in range(idx.shape[2]):
+                s = int(idx[b, t, j])
+                if 0 <= s < kv.shape[1]:
+                    out[b, t, j] = kv[b, s]
+    return out

@@ -160,3 +160,18 @@ def test_kv_append_rejects():
     assert app(S(n_k=16, key_dtype=1)) == EINVAL            # fp8 cache without scales
     assert app(s4, n_new=0, raw=None, tail=None, k=None) == tks.OK   # nothing to append
     assert app(S(batch=0, causal_ratio=4), raw=None, tail=None, k=None) == tks.OK
+
+
+def test_gather_rejects():
+    L = tks.lib()
+    g = lambda kv=A, b=2, n_kv=10, rb=64, idx=A, n_q=3, k=4, out=A: L.tks_gather_selected(
+        kv, b, n_kv, rb, idx, n_q, k, out, None)
+    assert g(rb=0) == EUNSUP
+    assert g(rb=24) == EUNSUP
+    assert g(rb=65552) == EUNSUP
+    assert g(idx=None) == EINVAL
+    assert g(out=None) == EINVAL
+    assert g(out=MIS) == EINVAL
+    assert g(kv=MIS) == EINVAL
+    assert g(n_q=-1) == EINVAL
+    assert g(k=0, idx=None, out=None) == tks.OK

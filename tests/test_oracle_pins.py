@@ -496,3 +496,22 @@ def test_materialized_score_tensor_size_is_256_gib():
     at S = 65,536 (2^16 * 64 * 2^14 * 4 bytes = 2^38 bytes)."""
     S, H, m = 65536, 64, 4
     assert S * H * (S // m) * 4 == 2 ** 38
+
+
+# ---------------------------------------------------------------- re-layout
+# (LongCat Sparse Attention abstract, strategy (1): the selected KV rows
+# copied into a contiguous layout.)
+
+def test_gather_equals_numpy_take_and_zero_fills_empty_slots():
+    rng = np.random.default_rng(40)
+    kv = rng.integers(0, 256, (2, 50, 48)).astype(np.uint8)
+    idx = rng.integers(0, 50, (2, 3, 7)).astype(np.int32)
+    got = oracle.gather_selected(kv, idx)
+    ref = np.take_along_axis(kv[:, None, :, :], idx[..., None].astype(np.int64), axis=2)
+    np.testing.assert_array_equal(got, ref)
+    idx[0, 1, 2] = -1
+    idx[1, 2, 0] = 50                               # outside [0, n_kv)
+    got = oracle.gather_selected(kv, idx)
+    assert (got[0, 1, 2] == 0).all() and (got[1, 2, 0] == 0).all()
+    ar = np.broadcast_to(np.arange(7, dtype=np.int32), (2, 1, 7))
+    np.testing.assert_array_equal(oracle.gather_selected(kv, ar)[:, 0], kv[:, :7])

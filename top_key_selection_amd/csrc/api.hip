@@ -649,6 +649,30 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
     return TKS_OK;
 }
 
+int tks_gather_selected(const void* kv, int32_t batch, int32_t n_kv, int32_t row_bytes,
+                        const int32_t* idx, int32_t n_q, int32_t topk, void* out,
+                        hipStream_t stream) {
+    if (batch < 0 || n_kv < 0 || n_q < 0 || topk < 0)
+        return fail(TKS_EINVAL, "negative size (batch %d, n_kv %d, n_q %d, topk %d)", batch, n_kv, n_q, topk);
+    if (row_bytes <= 0 || row_bytes % 16 != 0 || row_bytes > 65536)
+        return fail(TKS_EUNSUPPORTED, "row_bytes = %d (a multiple of 16, 16..65536)", row_bytes);
+    const int64_t rows = (int64_t)batch * n_q * topk;
+    if (rows == 0) return TKS_OK;
+    if ((int64_t)batch * n_q > INT32_MAX || rows * (row_bytes / 16) > ((int64_t)1 << 40))
+        return fail(TKS_EUNSUPPORTED, "output too large");
+    if (!idx || !aligned(idx, 4)) return fail(TKS_EINVAL, "idx is NULL or misaligned");
+    if (!out || !aligned(out, 16)) return fail(TKS_EINVAL, "out is NULL or not 16-byte aligned");
+    if (n_kv > 0 && (!kv || !aligned(kv, 16))) return fail(TKS_EINVAL, "kv is NULL or not 16-byte aligned");
+    tks::GatherArgs a{kv, idx, out, n_kv, n_q, topk, row_bytes};
+    hipError_t e;
+    {
+        Timed tm("gather", stream);
+        e = tks::launch_gather(a, rows, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    return TKS_OK;
+}
+
 int tks_profile_enable(int on) {
     std::lock_guard<std::mutex> g(g_prof_mu);
     if (on) prof_clear();
@@ -659,7 +683,7 @@ int tks_profile_enable(int on) {
 int tks_profile_read(const char* role, double* total_ms, int64_t* launches) {
     static const char* kRoles[] = {"score_flat",   "score_pooled",  "score_refine", "select_flat",
                                    "select_pooled", "select_refine", "select_scores", "pool",
-                                   "append"};
+                                   "append",       "gather"};
     if (!role || !total_ms || !launches) return fail(TKS_EINVAL, "NULL argument");
     bool known = false;
     for (const char* r : kRoles) known = known || strcmp(r, role) == 0;

@@ -92,6 +92,14 @@ struct AppendArgs {
     int32_t J0, n_jobs;
 };
 
+// Re-layout of selected rows (gather.hip): see tks_gather_selected.
+struct GatherArgs {
+    const void* kv;       // [batch, n_kv, row_bytes]
+    const int32_t* idx;   // [batch, n_q, topk]
+    void* out;            // [batch, n_q, topk, row_bytes]
+    int32_t n_kv, n_q, topk, row_bytes;
+};
+
 hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
                         hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream);
@@ -108,5 +116,6 @@ hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const Select
                                void* ws, hipStream_t stream);
 hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int dim, bool fp8, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, int64_t n_rows, hipStream_t stream);
 
 }  // namespace tks

@@ -52,7 +52,7 @@ SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat
            "tks_topk_flat", "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
            "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_kv_append",
-           "tks_profile_enable", "tks_profile_read")
+           "tks_gather_selected", "tks_profile_enable", "tks_profile_read")
 
 _lib = None
 
@@ -86,10 +86,11 @@ def lib() -> ctypes.CDLL:
     L.tks_hisa_refine_workspace.restype = sz
     L.tks_hisa_refine_topk.argtypes = [SP, P, P, P, P, i32, P, i32, i32, i32, P, P, P, sz, P]
     L.tks_kv_append.argtypes = [SP, P, i32, i32, P, P, P, i32, P, P]
+    L.tks_gather_selected.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
     L.tks_profile_enable.argtypes = [ctypes.c_int]
     L.tks_profile_read.argtypes = [ctypes.c_char_p, P, P]
     for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
-            L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append:
+            L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append, L.tks_gather_selected:
         s.restype = ctypes.c_int
     _lib = L
     return L
@@ -229,6 +230,24 @@ def kv_append(shape: Shape, raw, raw_len, k, k_scale=None, raw_tail=None, block=
     S = shape.c()
     _check(lib().tks_kv_append(ctypes.byref(S), _p(raw), raw.shape[1], int(raw_len), _p(raw_tail),
                                _p(k), _p(k_scale), int(block), _p(pooled), _stream()))
+
+
+def gather_selected(kv, idx, out=None):
+    """Rows kv[b, idx[b, t, j]] copied to a contiguous [batch, n_q, topk, ...]
+    buffer (zeros for -1).  kv: [batch, n_kv, ...] device tensor whose rows are
+    a multiple of 16 bytes; idx: int32 [batch, n_q, topk]."""
+    if not kv.is_cuda or not kv.is_contiguous() or not idx.is_cuda or not idx.is_contiguous():
+        raise ValueError("kv and idx must be contiguous device tensors")
+    if idx.dtype != torch.int32 or idx.dim() != 3 or idx.shape[0] != kv.shape[0]:
+        raise ValueError("idx must be int32 [batch, n_q, topk]")
+    batch, n_kv = kv.shape[0], kv.shape[1]
+    row_bytes = kv[0, 0].numel() * kv.element_size() if kv.numel() else 0
+    if out is None:
+        out = torch.empty((batch, idx.shape[1], idx.shape[2]) + tuple(kv.shape[2:]), dtype=kv.dtype,
+                          device=kv.device)
+    _check(lib().tks_gather_selected(_p(kv), batch, n_kv, row_bytes, _p(idx), idx.shape[1], idx.shape[2],
+                                     _p(out), _stream()))
+    return out
 
 
 def m_total_of(m_scored: int, force_flags: int) -> int:
