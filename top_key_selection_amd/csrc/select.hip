@@ -9,19 +9,26 @@
 //
 // Every candidate becomes the 64-bit composite (orderable score key << 32 |
 // ~index); the k largest composites are exactly the answer, whatever order
-// the candidates arrive in.  Selection runs in two passes over the row:
+// the candidates arrive in.  A row takes one of three routes:
 //
-//   1. a 4096-bin histogram of the top 12 bits of the score key (LDS, wave-
-//      aggregated atomics) locates the bin b* that holds the k-th score;
-//   2. one pass appends every candidate above b* to the selected list and
-//      every candidate in b* to a candidate list (both in LDS); the
-//      candidate list is sorted (bitonic) and its best k - |above| entries
-//      complete the selection, which is sorted and written.
+//   * at most 2048 candidates: all of them are gathered into LDS and sorted;
+//   * at least 16384 candidates: a threshold from a small sample of the row
+//     (the Indexer-TopK abstract on the StreamIndex page: estimate the score
+//     range from a sample, keep only candidates above a tight threshold,
+//     stay exact) fills an LDS pool in one pass;
+//   * otherwise a 4096-bin histogram of the top 12 bits of the score key
+//     (LDS, wave-aggregated atomics) locates the bin b* that holds the k-th
+//     score, and a second pass puts everything from b* up into the pool.
 //
-// A bin b* too large for the LDS candidate list (heavy exact ties) falls
-// back to an exact 8-bit radix select with an ordered tie scan, which needs
-// no buffer at all.  The passes keep four 16-byte loads per thread in
-// flight; when the rows are few (decode) a row gets a 1024-thread workgroup.
+// The best k of a pool are placed in order by counting on the score (4096
+// equal score bins, a scan of the bin counts, and each entry's rank inside
+// its bin), so selection and the final sort are one pass.  Pools that do
+// not fit, heavy exact ties and clustered scores keep the exact fallbacks:
+// LDS radix selection over 12- and 8-bit digits, an 8-bit radix select with
+// an ordered tie scan over the whole row (no buffer at all), and a bitonic /
+// merge sort.  Row passes keep four 16-byte loads per thread in flight;
+// when the rows are few (decode) a row gets a 1024-thread workgroup, and
+// few long rows are spread over every CU by a three-kernel form.
 //
 // Block-select output mode writes the kept blocks in ascending block order
 // with the forced first / local blocks added (score +inf).
