@@ -248,3 +248,32 @@ def gather_selected(kv, idx):
                 if 0 <= s < kv.shape[1]:
                     out[b, t, j] = kv[b, s]
     return out
+
+
+def sparse_attention(q, k, v, idx, scale):
+    """Attention of every query head over its selected keys only (HISA
+    abstract: the sparse attention reads only the selected entries; the
+    pages give no attention shapes, read here as one shared K / V head):
+        p_j = softmax over the valid slots j of scale * q[b, t, h] . k[b, idx_j]
+        o[b, t, h] = sum_j p_j v[b, idx_j]
+    Slots with idx outside [0, n_kv) (-1 padding) are not keys; a row with
+    no valid slot gives zeros.  q: [B, Tq, H, dk], k: [B, n_kv, dk],
+    v: [B, n_kv, dv] (float values), idx: int [B, Tq, topk].  fp64, plain
+    loops over (b, t)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    idx = np.asarray(idx)
+    B, T, H, _ = q.shape
+    out = np.zeros((B, T, H, v.shape[2]), np.float64)
+    for b in range(B):
+        for t in range(T):
+            sel = [int(s) for s in idx[b, t] if 0 <= int(s) < k.shape[1]]
+            if not sel:
+                continue
+            kk, vv = k[b, sel], v[b, sel]
+            s = scale * (q[b, t] @ kk.T)                 # [H, n_sel]
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            out[b, t] = (e / e.sum(axis=1, keepdims=True)) @ vv
+    return out

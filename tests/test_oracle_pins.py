@@ -515,3 +515,43 @@ def test_gather_equals_numpy_take_and_zero_fills_empty_slots():
     assert (got[0, 1, 2] == 0).all() and (got[1, 2, 0] == 0).all()
     ar = np.broadcast_to(np.arange(7, dtype=np.int32), (2, 1, 7))
     np.testing.assert_array_equal(oracle.gather_selected(kv, ar)[:, 0], kv[:, :7])
+
+
+# ------------------------------------------------------ sparse attention
+# (HISA abstract: the sparse attention that consumes the selected indices.)
+
+def test_sparse_attention_equals_torch_sdpa_when_every_key_is_selected():
+    rng = np.random.default_rng(50)
+    B, T, H, n, dk, dv = 2, 3, 4, 40, 16, 8
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, n, dk))
+    v = rng.standard_normal((B, n, dv))
+    idx = np.broadcast_to(rng.permutation(n).astype(np.int32), (B, T, n)).copy()
+    got = oracle.sparse_attention(q, k, v, idx, 0.3)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)                 # [B, H, T, dk]
+    kt = torch.from_numpy(k)[:, None].expand(B, H, n, dk)
+    vt = torch.from_numpy(v)[:, None].expand(B, H, n, dv)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.3)
+    np.testing.assert_allclose(got, ref.permute(0, 2, 1, 3).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_attention_closed_forms():
+    rng = np.random.default_rng(51)
+    B, T, H, n, dk, dv = 1, 2, 3, 30, 8, 5
+    k = rng.standard_normal((B, n, dk))
+    v = rng.standard_normal((B, n, dv))
+    idx = np.full((B, T, 6), -1, np.int32)
+    idx[0, 0, :4] = [3, 7, 11, 29]
+    idx[0, 1, 2] = 17                                   # one valid slot
+    # q = 0: every selected key weighs the same, o is the mean of their v
+    got = oracle.sparse_attention(np.zeros((B, T, H, dk)), k, v, idx, 1.0)
+    np.testing.assert_allclose(got[0, 0], np.broadcast_to(v[0, [3, 7, 11, 29]].mean(axis=0), (H, dv)))
+    np.testing.assert_allclose(got[0, 1], np.broadcast_to(v[0, 17], (H, dv)))
+    # slot order and padding do not matter; no valid slot gives zeros
+    q = rng.standard_normal((B, T, H, dk))
+    a = oracle.sparse_attention(q, k, v, idx, 0.5)
+    perm = idx.copy()
+    perm[0, 0] = idx[0, 0][::-1]
+    np.testing.assert_allclose(oracle.sparse_attention(q, k, v, perm, 0.5), a, rtol=1e-13)
+    none = np.full((B, T, 3), -1, np.int32)
+    assert (oracle.sparse_attention(q, k, v, none, 0.5) == 0).all()
