@@ -51,6 +51,8 @@ def parse():
                     help="skip the key-cache append measurement (bulk build + decode appends)")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the re-layout measurement of the selected latent KV rows")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the sparse attention measurement over the selected keys")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -434,6 +436,13 @@ def main():
     if not args.no_gather:
         ga = gather_bench(cfg, tks, dev, f_idx, ev)
 
+    # ---- the consumer: sparse attention of each query over the keys the flat
+    # top-k selected (synthetic shapes: 128 query heads over one shared bf16
+    # K / V head of width 128; the pages give none)
+    at = None
+    if not args.no_attention:
+        at = attention_bench(cfg, tks, dev, f_idx, ev)
+
     line = {
         "metric": METRIC, "value": value, "unit": "q-k scores/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -450,6 +459,7 @@ def main():
         "topk_standalone": ts,
         "kv_append": ka,
         "gather_selected": ga,
+        "sparse_attention": at,
     }
     print(json.dumps(line), flush=True)
 
@@ -556,6 +566,40 @@ def gather_bench(cfg, tks, dev, idx, ev, latent_dim=576):
     return dict(rows=int(idx.numel()), row_bytes=latent_dim * 2, ms=round(ms, 4), bytes=int(nbytes),
                 gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1),
                 frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
+def attention_bench(cfg, tks, dev, idx, ev, heads=128, dim=128):
+    """tks_sparse_attention of the step's queries over the keys the flat top-k
+    selected.  Bytes: the selected K and V rows read once, q read and the
+    fp32 output written; flops 4 * heads * dim per (query, selected key)."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(98)
+    q = torch.randn((cfg.batch, cfg.n_q, heads, dim), device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn((cfg.batch, cfg.n_k, dim), device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn((cfg.batch, cfg.n_k, dim), device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty((cfg.batch, cfg.n_q, heads, dim), dtype=torch.float32, device=dev)
+    ws = tks.workspace(tks.sparse_attention_workspace(cfg.batch, cfg.n_q, heads, cfg.topk), dev)
+    scale = dim ** -0.5
+    for _ in range(2):
+        tks.sparse_attention(q, k, v, idx, scale, out=out, ws=ws)
+    torch.cuda.synchronize()
+    tks.profile_enable(True)
+    reps = 10
+    for _ in range(reps):
+        tks.sparse_attention(q, k, v, idx, scale, out=out, ws=ws)
+    torch.cuda.synchronize()
+    tot, n = tks.profile_read("attend")
+    tks.profile_enable(False)
+    ms = tot / max(n, 1)
+    sel = int((idx >= 0).sum().item())
+    nbytes = sel * 2 * dim * 2 + q.numel() * 2 + out.numel() * 4
+    flops = 4.0 * heads * dim * sel
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return dict(heads=heads, dim=dim, selected=sel, ms=round(ms, 4), bytes=int(nbytes),
+                gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                tflop_per_s=round(flops / (ms * 1e-3) / 1e12, 2))
 
 
 def cpu_baseline(cfg, k_np, ks_np, nvis, target_s):

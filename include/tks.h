@@ -228,6 +228,28 @@ int tks_gather_selected(const void* kv, int32_t batch, int32_t n_kv, int32_t row
                         hipStream_t stream);
 
 /*
+ * Sparse attention over the selected keys (HISA abstract: the sparse
+ * attention consumes the per-query index set and reads only those
+ * entries).  The pages give no attention shapes; this form has H query
+ * heads over one shared K / V head of width 128:
+ *     p_j = softmax over the valid slots j of scale * q[b,t,h,:] . k[b,idx_j,:]
+ *     out[b,t,h,:] = sum_j p_j v[b,idx_j,:]
+ * Slots with idx = -1 or outside [0, n_kv) are ignored; a row without a
+ * valid slot gives zeros.  Scores and the softmax run in fp32, the weights
+ * enter P.V as bf16.
+ *   q:   bf16 [batch, n_q, heads, 128];  k, v: bf16 [batch, n_kv, 128];
+ *   idx: int32 [batch, n_q, topk];        out: fp32 [batch, n_q, heads, 128].
+ * heads must be a multiple of 16 (16..128), dim 128, 1 <= topk <= 2048.
+ * workspace: tks_sparse_attention_workspace bytes, 256-byte aligned
+ * (per-split partial outputs).
+ */
+size_t tks_sparse_attention_workspace(int32_t batch, int32_t n_q, int32_t heads, int32_t topk);
+int tks_sparse_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t n_q,
+                         int32_t heads, int32_t dim, int32_t n_kv, const int32_t* idx,
+                         int32_t topk, float scale, float* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Kernel timing instrumentation (for benchmarks and profiling).  While
  * enabled, every kernel launch the library makes is bracketed by a pair of
  * HIP events recorded on the launch's stream.  tks_profile_enable(1) clears
@@ -243,6 +265,7 @@ int tks_gather_selected(const void* kv, int32_t batch, int32_t n_kv, int32_t row
  *   "pool"          -- tks_hisa_pool_keys
  *   "append"        -- tks_kv_append
  *   "gather"        -- tks_gather_selected
+ *   "attend"        -- tks_sparse_attention
  * Returns TKS_EINVAL for an unknown role or NULL outputs.
  */
 int tks_profile_enable(int on);

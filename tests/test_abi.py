@@ -175,3 +175,26 @@ def test_gather_rejects():
     assert g(kv=MIS) == EINVAL
     assert g(n_q=-1) == EINVAL
     assert g(k=0, idx=None, out=None) == tks.OK
+
+
+def test_sparse_attention_rejects():
+    L = tks.lib()
+
+    def att(q=A, k=A, v=A, b=2, nq=1, h=64, d=128, nkv=100, idx=A, topk=16, scale=0.1, out=A, ws=A,
+            wsb=1 << 30):
+        return L.tks_sparse_attention(q, k, v, b, nq, h, d, nkv, idx, topk, scale, out, ws, wsb, None)
+
+    assert att(h=8) == EUNSUP
+    assert att(h=40) == EUNSUP
+    assert att(h=144) == EUNSUP
+    assert att(d=64) == EUNSUP
+    assert att(topk=0) == EUNSUP
+    assert att(topk=2049) == EUNSUP
+    assert att(scale=float("nan")) == EINVAL
+    assert att(q=MIS) == EINVAL
+    assert att(idx=None) == EINVAL
+    assert att(out=None) == EINVAL
+    assert att(ws=None) == EWS
+    assert att(wsb=16) == EWS
+    assert att(b=0, q=None, k=None, v=None, idx=None, out=None, ws=None) == tks.OK
+    assert tks.sparse_attention_workspace(2, 1, 64, 2048) >= 2 * 8 * 64 * 128 * 4

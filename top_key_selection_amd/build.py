@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtks.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "pool.hip", "append.hip", "gather.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "pool.hip", "append.hip", "gather.hip", "attend.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -673,6 +673,60 @@ int tks_gather_selected(const void* kv, int32_t batch, int32_t n_kv, int32_t row
     return TKS_OK;
 }
 
+size_t tks_sparse_attention_workspace(int32_t batch, int32_t n_q, int32_t heads, int32_t topk) {
+    if (batch < 0 || n_q < 0 || heads < 16 || heads > 128 || heads % 16 || topk < 1 || topk > kMaxTopk)
+        return 0;
+    return tks::attend_workspace((int64_t)batch * n_q, heads, topk);
+}
+
+int tks_sparse_attention(const void* q, const void* k, const void* v, int32_t batch, int32_t n_q,
+                         int32_t heads, int32_t dim, int32_t n_kv, const int32_t* idx,
+                         int32_t topk, float scale, float* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    if (batch < 0 || n_q < 0 || n_kv < 0)
+        return fail(TKS_EINVAL, "negative size (batch %d, n_q %d, n_kv %d)", batch, n_q, n_kv);
+    if (heads < 16 || heads > 128 || heads % 16)
+        return fail(TKS_EUNSUPPORTED, "heads = %d (a multiple of 16, 16..128)", heads);
+    if (dim != 128) return fail(TKS_EUNSUPPORTED, "dim = %d (supported 128)", dim);
+    if (topk < 1 || topk > kMaxTopk) return fail(TKS_EUNSUPPORTED, "topk = %d (supported 1..%d)", topk, kMaxTopk);
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(TKS_EINVAL, "scale is not finite");
+    const int64_t rows = (int64_t)batch * n_q;
+    if (rows == 0) return TKS_OK;
+    if (rows > INT32_MAX / heads) return fail(TKS_EUNSUPPORTED, "batch * n_q * heads exceeds 2^31 - 1");
+    if (!q || !aligned(q, 16)) return fail(TKS_EINVAL, "q is NULL or not 16-byte aligned");
+    if (n_kv > 0 && (!k || !v || !aligned(k, 16) || !aligned(v, 16)))
+        return fail(TKS_EINVAL, "k / v NULL or not 16-byte aligned");
+    if (!idx || !aligned(idx, 4)) return fail(TKS_EINVAL, "idx is NULL or misaligned");
+    if (!out || !aligned(out, 4)) return fail(TKS_EINVAL, "out is NULL or misaligned");
+    const size_t need = tks::attend_workspace(rows, heads, topk);
+    if (!workspace || workspace_bytes < need)
+        return fail(TKS_EWORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0, need);
+    if (!aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
+    tks::AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.idx = idx;
+    a.n_split = tks::attend_splits(topk);
+    const int64_t part = rows * a.n_split * heads;
+    a.o_part = static_cast<float*>(workspace);
+    a.ml_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(part * 128 * 4, 256));
+    a.out = out;
+    a.n_q = n_q;
+    a.heads = heads;
+    a.n_kv = n_kv;
+    a.topk = topk;
+    a.scale = scale;
+    hipError_t e;
+    {
+        Timed tm("attend", stream);
+        e = tks::launch_attend(a, rows, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return TKS_OK;
+}
+
 int tks_profile_enable(int on) {
     std::lock_guard<std::mutex> g(g_prof_mu);
     if (on) prof_clear();
@@ -683,7 +737,7 @@ int tks_profile_enable(int on) {
 int tks_profile_read(const char* role, double* total_ms, int64_t* launches) {
     static const char* kRoles[] = {"score_flat",   "score_pooled",  "score_refine", "select_flat",
                                    "select_pooled", "select_refine", "select_scores", "pool",
-                                   "append",       "gather"};
+                                   "append",       "gather",        "attend"};
     if (!role || !total_ms || !launches) return fail(TKS_EINVAL, "NULL argument");
     bool known = false;
     for (const char* r : kRoles) known = known || strcmp(r, role) == 0;

@@ -100,6 +100,19 @@ struct GatherArgs {
     int32_t n_kv, n_q, topk, row_bytes;
 };
 
+// Sparse attention over selected keys (attend.hip): see tks_sparse_attention.
+struct AttnArgs {
+    const uint16_t* q;    // bf16 [rows, heads, 128]
+    const uint16_t* k;    // bf16 [batch, n_kv, 128]
+    const uint16_t* v;    // bf16 [batch, n_kv, 128]
+    const int32_t* idx;   // [rows, topk]
+    float* o_part;        // [rows, n_split, heads, 128]
+    float* ml_part;       // [rows, n_split, heads, 2]
+    float* out;           // [rows, heads, 128]
+    int32_t n_q, heads, n_kv, topk, n_split;
+    float scale;
+};
+
 hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
                         hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream);
@@ -117,5 +130,8 @@ hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const Select
 hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int dim, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int64_t n_rows, hipStream_t stream);
+size_t attend_workspace(int64_t rows, int32_t heads, int32_t topk);
+int32_t attend_splits(int32_t topk);
+hipError_t launch_attend(const AttnArgs& a, int64_t rows, hipStream_t stream);
 
 }  // namespace tks

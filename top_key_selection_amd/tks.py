@@ -52,7 +52,8 @@ SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat
            "tks_topk_flat", "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
            "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_kv_append",
-           "tks_gather_selected", "tks_profile_enable", "tks_profile_read")
+           "tks_gather_selected", "tks_sparse_attention_workspace", "tks_sparse_attention",
+           "tks_profile_enable", "tks_profile_read")
 
 _lib = None
 
@@ -87,10 +88,14 @@ def lib() -> ctypes.CDLL:
     L.tks_hisa_refine_topk.argtypes = [SP, P, P, P, P, i32, P, i32, i32, i32, P, P, P, sz, P]
     L.tks_kv_append.argtypes = [SP, P, i32, i32, P, P, P, i32, P, P]
     L.tks_gather_selected.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
+    L.tks_sparse_attention_workspace.argtypes = [i32, i32, i32, i32]
+    L.tks_sparse_attention_workspace.restype = sz
+    L.tks_sparse_attention.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, i32, ctypes.c_float, P, P, sz, P]
     L.tks_profile_enable.argtypes = [ctypes.c_int]
     L.tks_profile_read.argtypes = [ctypes.c_char_p, P, P]
     for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
-            L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append, L.tks_gather_selected:
+            L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append, L.tks_gather_selected, \
+            L.tks_sparse_attention:
         s.restype = ctypes.c_int
     _lib = L
     return L
@@ -250,6 +255,26 @@ def gather_selected(kv, idx, out=None):
     return out
 
 
+def sparse_attention_workspace(batch, n_q, heads, topk) -> int:
+    return int(lib().tks_sparse_attention_workspace(batch, n_q, heads, topk))
+
+
+def sparse_attention(q, k, v, idx, scale, out=None, ws=None):
+    """fp32 [batch, n_q, heads, 128]: attention of q over the keys idx selects.
+    q bf16 [batch, n_q, heads, 128]; k, v bf16 [batch, n_kv, 128]; idx int32
+    [batch, n_q, topk]."""
+    _dev(q, "q", _BF16), _dev(k, "k", _BF16), _dev(v, "v", _BF16), _dev(idx, "idx", (torch.int32,))
+    batch, n_q, heads, dim = q.shape
+    topk = idx.shape[2]
+    if out is None:
+        out = torch.empty((batch, n_q, heads, dim), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(sparse_attention_workspace(batch, n_q, heads, topk), q.device)
+    _check(lib().tks_sparse_attention(_p(q), _p(k), _p(v), batch, n_q, heads, dim, k.shape[1], _p(idx), topk,
+                                      float(scale), _p(out), _p(ws), ws.numel(), _stream()))
+    return out
+
+
 def m_total_of(m_scored: int, force_flags: int) -> int:
     return m_scored + bin(force_flags & 3).count("1")
 
@@ -315,7 +340,7 @@ def hisa_topk(shape: Shape, q, w, k, k_scale, block, m_scored, force_flags, topk
 
 
 PROFILE_ROLES = ("score_flat", "score_pooled", "score_refine", "select_flat", "select_pooled",
-                 "select_refine", "select_scores", "pool")
+                 "select_refine", "select_scores", "pool", "append", "gather", "attend")
 
 
 def profile_enable(on: bool = True):
