@@ -1016,6 +1016,9 @@ __device__ __forceinline__ void setup_row(const SelectArgs& a, RowCtx& r, Select
 
 // ------------------------------------------------- one workgroup per row
 
+template <int NT>
+__device__ __forceinline__ int32_t pool_best(SelectLds& L, int32_t n_pool, int32_t K, bool& sorted);
+
 // Exact selection by a full histogram of the row (the path that never
 // fails): the row's top-K candidates into L.u[0, n) (unsorted); returns n.
 template <bool VEC, int NT>
