@@ -6,7 +6,7 @@
 //     o[h] = sum_j p_j v[idx_j]
 //
 // Split-K decoding: a workgroup owns one query row, 64 heads (16 per wave)
-// and one split of 256 slots, walked in chunks of 64 slots (the next
+// and one split of 256 slots, walked in chunks of 32 slots (the next
 // chunk's rows load into registers while the current one is computed).  A chunk's key
 // rows go to LDS (16-byte pieces, XOR-swizzled by row so the MFMA operand
 // reads are conflict free) and its value rows to a transposed LDS tile
@@ -15,7 +15,9 @@
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_bf16, keys as rows, heads as columns,
 //                   so a head's scores sit in one lane column and its max /
 //                   sum need two lane exchanges;
-//   online softmax  exp2 with the running max, O rescaled per head;
+//   online softmax  exp2 against a reference moved only when a score exceeds
+//                   it by more than 8 (O, l rescaled then), so most chunks
+//                   skip the rescale;
 //   O += P . V      P (bf16) is already in the A-operand layout once the
 //                   key order of a 32-key step is permuted, and V is read in
 //                   that order.
@@ -30,15 +32,15 @@ namespace tks {
 namespace {
 
 constexpr int kD = 128;          // key / value width
-constexpr int kChunk = 64;       // slots per LDS chunk
+constexpr int kChunk = 32;       // slots per LDS chunk
 constexpr int kSplit = 256;      // slots per workgroup
-constexpr int kVtStride = 72;    // bf16 per transposed value row (64 + 8 pad)
+constexpr int kVtStride = kChunk + 8;  // bf16 per transposed value row (padded)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void attend_split_kernel(AttnArgs a) {
-    __shared__ __align__(16) uint8_t s_k[kChunk * kD * 2];          // 16 KiB, swizzled rows
-    __shared__ __align__(16) __bf16 s_vt[kD * kVtStride];          // 18 KiB, transposed
+__global__ __launch_bounds__(256, 4) void attend_split_kernel(AttnArgs a) {
+    __shared__ __align__(16) uint8_t s_k[kChunk * kD * 2];          // swizzled key rows
+    __shared__ __align__(16) __bf16 s_vt[kD * kVtStride];          // transposed value rows
     __shared__ int32_t s_valid[kChunk];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -65,29 +67,32 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttnArgs a) {
     float m_run = -__builtin_inff(), l_run = 0.0f;  // of head head0 + c16
 
     const float sl2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
-    // a chunk is 64 rows x 16 pieces for K and for V: 4 + 4 per thread, loaded
-    // into registers one chunk ahead of its use.  Wave w takes pieces
+    // a chunk is kChunk rows x 16 pieces for K and for V: PT + PT per thread,
+    // loaded into registers one chunk ahead of its use.  Wave w takes pieces
     // 4w .. 4w+3 of every row, 16 rows per instruction: the transposed value
     // writes then spread over 16 banks (4-way), the key writes over all.
-    u32x4 kr[4], vr4[4];
-    bool okr[4];
+    constexpr int PT = kChunk / 16;  // pieces per thread and chunk
+    u32x4 kr[PT], vr4[PT];
+    bool okr[PT];
     auto load_chunk = [&](int32_t c0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < PT; ++i) {
             const int r = 16 * i + (lane & 15), c = 4 * wave + (lane >> 4);
             const int32_t slot = c0 + r;
             const int32_t key = slot < slot_end ? idx_row[slot] : -1;
             okr[i] = key >= 0 && key < a.n_kv;
+            // an empty slot reads key 0 (branch-free): its score is masked,
+            // so its weight is 0 and its (finite) value row adds nothing
             const int64_t base = ((int64_t)b * a.n_kv + (okr[i] ? key : 0)) * kD + c * 8;
-            kr[i] = okr[i] ? *reinterpret_cast<const u32x4*>(a.k + base) : u32x4{0, 0, 0, 0};
-            vr4[i] = okr[i] ? *reinterpret_cast<const u32x4*>(a.v + base) : u32x4{0, 0, 0, 0};
+            kr[i] = *reinterpret_cast<const u32x4*>(a.k + base);
+            vr4[i] = *reinterpret_cast<const u32x4*>(a.v + base);
         }
     };
-    if (slot0 < slot_end) load_chunk(slot0);
+    if (slot0 < slot_end && a.n_kv > 0) load_chunk(slot0);
     for (int32_t c0 = slot0; c0 < slot_end; c0 += kChunk) {
         __syncthreads();  // the previous chunk's operands have been read
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < PT; ++i) {
             const int r = 16 * i + (lane & 15), c = 4 * wave + (lane >> 4);
             *reinterpret_cast<u32x4*>(s_k + r * (kD * 2) + ((c ^ (r & 15)) * 16)) = kr[i];
             const bf16x8 vb = __builtin_bit_cast(bf16x8, vr4[i]);
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttnArgs a) {
             if (c == 0) s_valid[r] = okr[i] ? 1 : 0;
         }
         __syncthreads();
-        if (c0 + kChunk < slot_end) load_chunk(c0 + kChunk);  // in flight during this chunk
+        if (c0 + kChunk < slot_end && a.n_kv > 0) load_chunk(c0 + kChunk);  // in flight during this chunk
         if (!active) continue;
 
         // S^T: keys 16 mt + 4 g + i (rows) x heads c16 (columns)
@@ -113,7 +118,11 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttnArgs a) {
                 s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], s[mt], 0, 0, 0);
             }
         }
-        // online softmax of head c16 over this chunk
+        // online softmax of head c16 over this chunk, with a lazily moved
+        // reference: the weights are 2^(s - m_run), and m_run (and O, l with
+        // it) is only moved when a score exceeds it by more than 8, so the
+        // weights stay below 2^8 and most chunks need no rescaling.  The
+        // final normalisation makes the result independent of m_run.
         float cmax = -__builtin_inff();
 #pragma unroll
         for (int mt = 0; mt < kChunk / 16; ++mt)
@@ -125,32 +134,37 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttnArgs a) {
             }
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(m_run, cmax);
-        // (no valid key yet: m_new = -inf, every p is 0 and nothing rescales)
-        const float alpha = m_new == -__builtin_inff() ? 1.0f : exp2f(m_run - m_new);
+        // a chunk without a valid key (the same for every head) adds nothing
+        if (cmax == -__builtin_inff()) continue;
+        // the wave moves its references together (one branch for all heads)
+        const bool move = cmax > m_run + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float m_new = move ? cmax : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // m_run = -inf: 0
+            l_run *= alpha;
+            m_run = m_new;
+            // O rows are heads 4 g + i: their alpha sits in lane column 4 g + i
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+            for (int dt = 0; dt < kD / 16; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[dt][i] *= al[i];
+        }
         float psum = 0.0f;
         bf16x8 pa[kChunk / 32];
 #pragma unroll
         for (int mt = 0; mt < kChunk / 16; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = m_new == -__builtin_inff() ? 0.0f : exp2f(s[mt][i] - m_new);
-                const __bf16 pb = (__bf16)p;
+                const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(s[mt][i] - m_run);
                 psum += (float)pb;  // the sum of the weights P.V uses
                 pa[mt >> 1][(mt & 1) * 4 + i] = pb;
             }
         psum += __shfl_xor(psum, 16);
         psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        // O rows are heads 4 g + i: their alpha sits in lane column 4 g + i
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-        for (int dt = 0; dt < kD / 16; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[dt][i] *= al[i];
+        l_run += psum;
         // O += P . V; step kk covers keys 32 kk .. + 31, lane group g holding
         // keys 32 kk + 4 g + 0..3 and 32 kk + 16 + 4 g + 0..3
 #pragma unroll
