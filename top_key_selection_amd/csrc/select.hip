@@ -490,8 +490,8 @@ __device__ __forceinline__ void sort_desc(uint64_t* u, uint64_t* tmp, int32_t n)
 
 // The best K of src[0, n) (distinct composites), sorted descending, into
 // out[0, min(K, n)), by counting on the score: the score range [vmin, vmax]
-// is cut into 4096 equal bins (fp32 (v - vmin) * scale, a non-decreasing
-// map of the score), each entry is scattered to its bin's run (bins in
+// is cut into NB equal bins (fp32 (v - vmin) * scale, a non-decreasing map
+// of the score; 4096 unless the list is short), each entry is scattered to its bin's run (bins in
 // descending order, run starts from an exclusive scan of the bin counts),
 // and inside a bin its place is the number of bin entries above it in the
 // total order (independent LDS reads, no dependency chain); entries placed
@@ -503,13 +503,14 @@ __device__ __forceinline__ void sort_desc(uint64_t* u, uint64_t* tmp, int32_t n)
 constexpr int kSortBins = 4096;
 constexpr int kBinCap = 128;
 
-template <int NT, int NMAX>
+template <int NT, int NMAX, int NB = kSortBins>
 __device__ __forceinline__ bool counting_topk(SelectLds& L, const uint64_t* src, int32_t n, int32_t K,
                                               uint64_t* out, uint64_t* tmp, uint32_t* bins) {
     constexpr int W = NT / kWave;
     constexpr int EPT = (NMAX + NT - 1) / NT;
-    constexpr int per = kSortBins / NT;  // bins per thread in the scan, descending
+    constexpr int per = NB >= NT ? NB / NT : 1;  // bins per thread in the scan, descending
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool has = NB >= NT || tid < NB;
     uint64_t e[EPT];
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -530,7 +531,7 @@ __device__ __forceinline__ bool counting_topk(SelectLds& L, const uint64_t* src,
         L.hist8[wave] = kmin;
         L.hist8[64 + wave] = kmax;
     }
-    for (int i = tid; i < kSortBins; i += NT) bins[i] = 0u;
+    for (int i = tid; i < NB; i += NT) bins[i] = 0u;
     __syncthreads();
     kmin = L.hist8[0];
     kmax = L.hist8[64];
@@ -544,12 +545,12 @@ __device__ __forceinline__ bool counting_topk(SelectLds& L, const uint64_t* src,
         __syncthreads();
         return false;
     }
-    const float scale = vspan > 0.0f ? (float)(kSortBins - 1) / vspan : 0.0f;
+    const float scale = vspan > 0.0f ? (float)(NB - 1) / vspan : 0.0f;
     uint32_t bin[EPT], rank[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const float v = key_score((uint32_t)(e[i] >> 32));
-        bin[i] = min((uint32_t)((v - vmin) * scale), (uint32_t)(kSortBins - 1));
+        bin[i] = min((uint32_t)((v - vmin) * scale), (uint32_t)(NB - 1));
         rank[i] = tid + i * NT < n ? atomicAdd(&bins[bin[i]], 1u) : 0u;
     }
     __syncthreads();
@@ -559,7 +560,7 @@ __device__ __forceinline__ bool counting_topk(SelectLds& L, const uint64_t* src,
     uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
-        c[i] = bins[kSortBins - 1 - (per * tid + i)];
+        c[i] = has ? bins[NB - 1 - (per * tid + i)] : 0u;
         sum += (int32_t)c[i];
         mx = max(mx, c[i]);
     }
@@ -587,7 +588,7 @@ __device__ __forceinline__ bool counting_topk(SelectLds& L, const uint64_t* src,
     }
 #pragma unroll
     for (int i = 0; i < per; ++i) {
-        bins[kSortBins - 1 - (per * tid + i)] = (uint32_t)run;
+        if (has) bins[NB - 1 - (per * tid + i)] = (uint32_t)run;
         run += (int32_t)c[i];
     }
     __syncthreads();
@@ -621,9 +622,13 @@ static_assert(kMaxK * 8 + kSortBins * 4 <= kCap * 8, "counting scratch fits the 
 template <int NT>
 __device__ __forceinline__ void sort_final(SelectLds& L, int32_t n) {
     if (n <= 1) return;
-    if (!counting_topk<NT, kMaxK>(L, L.u, n, n, L.u, &L.u[kMaxK],
-                                  reinterpret_cast<uint32_t*>(&L.u[kMaxK + kMaxK])))
-        sort_desc<NT>(L.u, &L.u[kMaxK], n);
+    uint32_t* bins = reinterpret_cast<uint32_t*>(&L.u[kMaxK + kMaxK]);
+    // about two bins per entry: short lists (block selection) zero and
+    // scan far fewer counters
+    const bool ok = n <= 256    ? counting_topk<NT, kMaxK, 512>(L, L.u, n, n, L.u, &L.u[kMaxK], bins)
+                    : n <= 1024 ? counting_topk<NT, kMaxK, 2048>(L, L.u, n, n, L.u, &L.u[kMaxK], bins)
+                                : counting_topk<NT, kMaxK>(L, L.u, n, n, L.u, &L.u[kMaxK], bins);
+    if (!ok) sort_desc<NT>(L.u, &L.u[kMaxK], n);
 }
 
 // Write a finished row: sel[0, n_sel) sorted descending on the composite.
