@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
     // Slots past `limit` are certainly masked.
     int32_t limit = slot_end;
     if (!BLOCKS) limit = min(slot_end, max(0, a.vis.count(t) - a.col_key0));
-    const int32_t work_end = a.write_masked ? slot_end : limit;
+    int32_t work_end = a.write_masked ? slot_end : limit;
     if (slot_begin >= work_end) return;
 
     // q fragment: A operand rows = heads (mb*32 + m), k elements as above.
@@ -145,11 +145,30 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
     // the row's block list, staged in LDS: a key address then never waits on
     // a global load that the key loads already in flight would hold up
     __shared__ int32_t s_blk[BLOCKS ? kMaxBlkEntries : 1];
+    __shared__ int32_t s_last[4];
     if constexpr (BLOCKS) {
         const int32_t* blk_row = a.blk + (a.rows.y0 + y) * a.blk_stride;
         const int32_t n_ent = (a.n_cols + bmask) >> a.block_shift;
-        for (int i = threadIdx.x; i < n_ent; i += 256) s_blk[i] = blk_row[i];
+        int32_t last = -1;  // last list entry holding a block
+        for (int i = threadIdx.x; i < n_ent; i += 256) {
+            const int32_t bb = blk_row[i];
+            s_blk[i] = bb;
+            if (bb >= 0) last = i;
+        }
+        if constexpr (!WPR) {
+            // slots after the last kept block (the -1 padding of rows with
+            // fewer eligible blocks than the list holds) need no work
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
+            if (lane == 0) s_last[wave] = last;
+        }
         __syncthreads();
+        if constexpr (!WPR) {
+            last = max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3]));
+            limit = min(limit, (last + 1) << a.block_shift);
+            if (!a.write_masked) work_end = limit;
+            if (slot_begin >= work_end) return;
+        }
     }
 
     auto key_of = [&](int32_t slot, bool& valid) -> int32_t {
