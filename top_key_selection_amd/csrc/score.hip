@@ -524,10 +524,13 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
 // Keys shared by a block of queries (prefill: contiguous key runs, bf16
 // keys, D = 128).  A workgroup of NW waves owns NW consecutive query rows
 // of one sequence, one row per wave, and a run of key slots.  The run is
-// staged through an LDS ring of 64-key stages that all waves fill together
+// staged through an LDS ring of 128-key stages that all waves fill together
 // with direct global->LDS copies; every staged key feeds the MFMAs of all NW
 // queries, so a key crosses the L2 once per NW queries instead of once per
-// query, and the copies run NS - 1 stages ahead of the MFMAs.
+// query, and the copies run NS - 1 stages ahead of the MFMAs.  The loop
+// walks one stage per barrier with its four sub-blocks unrolled, so every
+// sub-block's LDS reads carry its offset as an immediate; the waves raise
+// their issue priority while they feed the matrix pipe.
 //
 // Stage layout: key row r (256 bytes = 16 chunks of 16 bytes) keeps logical
 // chunk c at physical chunk c ^ (r & 15).  A copy writes LDS linearly (lane
@@ -538,9 +541,9 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
 // the reads are free of bank conflicts.
 struct SharedRing {
     static constexpr int D = 128;
-    static constexpr int SK = 64;            // keys per stage
+    static constexpr int SK = 128;            // keys per stage
     static constexpr int SPS = SK / 32;       // 32-key sub-blocks per stage
-    static constexpr int STAGE = SK * D * 2;  // 16 KiB
+    static constexpr int STAGE = SK * D * 2;  // 32 KiB
     static constexpr int NS = 3;              // stages in flight
 };
 constexpr int kSharedRows = 8;  // query rows (waves) per workgroup
@@ -556,24 +559,6 @@ __device__ __forceinline__ float add_upper_half(float x) {
 #else
     return x;
 #endif
-}
-
-// Read the 8 B-operand chunks of one 32-key sub-block with a single wait.
-__device__ __forceinline__ void lds_read_sub(uint32_t base, const uint32_t* off, u32x4* raw) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(raw[4]),
-          "=&v"(raw[5]), "=&v"(raw[6]), "=&v"(raw[7])
-        : "v"(base + off[0]), "v"(base + off[1]), "v"(base + off[2]), "v"(base + off[3]),
-          "v"(base + off[4]), "v"(base + off[5]), "v"(base + off[6]), "v"(base + off[7]));
 }
 
 template <int MB, int NW>
@@ -678,16 +663,28 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
         if (s + RG::NS - 1 < n_st) fetch(s + RG::NS - 1);
     };
     static_assert(RG::NS == 3, "sync() counts one later stage");
-    static_assert(RG::SPS % 2 == 0, "sub-block pairs never straddle a stage");
+    static_assert(RG::SPS % 2 == 0, "a sub-block's accumulator set (u % 2) follows from its place in the stage");
 
     uint32_t roff[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) roff[ks] = m * (2 * D) + (((hf * 8 + ks) ^ (m & 15)) * 16);
-    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    auto mfma_sub = [&](int32_t u, f32x16* acc) {
+    // this lane's chunk pointers into the current stage; a sub-block adds a
+    // compile-time offset, which the LDS reads carry as an immediate
+    const uint8_t* sp[KS];
+    auto stage_ptrs = [&](int32_t st) {
+        const uint8_t* b = ring + (st % RG::NS) * RG::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sp[ks] = b + roff[ks];
+    };
+    auto read_sub = [&](int j, u32x4* raw) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            raw[ks] = *reinterpret_cast<const u32x4*>(sp[ks] + j * 32 * (2 * D));
+    };
+    auto mfma_sub = [&](int j, f32x16* acc) {
         u32x4 raw[KS];
-        lds_read_sub(ring_addr + ((u / RG::SPS) % RG::NS) * RG::STAGE + (u % RG::SPS) * 32 * (2 * D),
-                     roff, raw);
+        read_sub(j, raw);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -708,21 +705,16 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
             for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
         return add_upper_half(sc);
     };
-    // MFMAs of sub-block u into `acc`, with the ReLU * w reduction of the
-    // previous sub-block (`prev`) spread between them in program order: each
-    // k-step's MFMAs are followed by the next slice of the reduction, fenced
-    // so the scheduler keeps the interleave and the vector work issues while
-    // the matrix pipe is busy.  The reduction order is that of reduce().
-    auto mfma_reduce = [&](int32_t u, f32x16* acc, const f32x16* prev) {
+    auto mfma_reduce = [&](int j, f32x16* acc, const f32x16* prev) {
         constexpr int PER = MB * 16 / KS;  // reduced elements per k-step
         u32x4 raw[KS];
-        lds_read_sub(ring_addr + ((u / RG::SPS) % RG::NS) * RG::STAGE + (u % RG::SPS) * 32 * (2 * D),
-                     roff, raw);
+        read_sub(j, raw);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
         float sc = 0.0f;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 kb = __builtin_bit_cast(bf16x8, raw[ks]);
@@ -735,44 +727,52 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
                 sc = fmaf(wv[e >> 4][e & 15], relu_bits(prev[e >> 4][e & 15]), sc);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         return add_upper_half(sc);
     };
     float* orow = a.out + y * a.out_stride;
     auto store = [&](int32_t u, float sc) {
         const int32_t slot = slot_begin + u * 32 + m;
-        if (active && hf == 0 && slot < slot_end) {
-            if (slot < limit)
-                orow[slot] = sc;
-            else if (a.write_masked)
-                orow[slot] = -__builtin_inff();
-        }
+        const bool vis = slot < limit;
+        if (active && hf == 0 && slot < slot_end && (vis || a.write_masked))
+            orow[slot] = vis ? sc : -__builtin_inff();
     };
 
 #pragma unroll
     for (int s = 0; s < RG::NS - 1; ++s)
         if (s < n_st) fetch(s);
-    // Sub-block u is part u % SPS of stage u / SPS.  The MFMAs of u + 1 are
-    // issued together with the VALU reduction of u (two accumulator sets),
-    // and the store of an even sub-block waits until after a following
-    // barrier so that the stage waits never cover a store just issued.
+    // Sub-block u is part u % SPS of stage u / SPS.  The MFMAs of u are
+    // issued together with the VALU reduction of u - 1 (two accumulator
+    // sets, acc[u % 2]); a stage's first sub-block follows its barrier, and
+    // the store of the sub-block before it comes after that barrier so that
+    // the stage waits never cover a store just issued.
     f32x16 acc0[MB], acc1[MB];
     sync(0);
+    stage_ptrs(0);
     mfma_sub(0, acc0);
-    int32_t u = 0;
-    for (; u + 2 < nsub; u += 2) {
-        const float s0 = mfma_reduce(u + 1, acc1, acc0);
-        if ((u + 2) % RG::SPS == 0) sync((u + 2) / RG::SPS);
-        store(u, s0);
-        const float s1 = mfma_reduce(u + 2, acc0, acc1);
-        store(u + 1, s1);
+    for (int32_t st = 0;; ++st) {
+        if (st > 0) {
+            if (st * RG::SPS >= nsub) break;
+            sync(st);
+            stage_ptrs(st);
+        }
+        bool end = false;
+#pragma unroll
+        for (int j = 0; j < RG::SPS; ++j) {
+            const int32_t u = st * RG::SPS + j;
+            if (!end && u > 0) {
+                if (u >= nsub) {
+                    end = true;
+                } else {
+                    const float sv = (j & 1) ? mfma_reduce(j, acc1, acc0) : mfma_reduce(j, acc0, acc1);
+                    store(u - 1, sv);
+                }
+            }
+        }
+        if (end) break;
     }
-    if (u + 1 < nsub) {
-        mfma_sub(u + 1, acc1);
-        store(u, reduce(acc0));
-        store(u + 1, reduce(acc1));
-    } else {
-        store(u, reduce(acc0));
-    }
+    // the last sub-block's reduction
+    store(nsub - 1, ((nsub - 1) & 1) ? reduce(acc1) : reduce(acc0));
     wait_vmcnt<0>();
 }
 
