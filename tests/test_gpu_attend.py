@@ -40,6 +40,7 @@ def check(o, ref, vmax, what):
     (2, 2, 128, 1000, 300),
     (1, 3, 48, 5000, 2048),
     (3, 1, 32, 64, 1),
+    (1, 2, 112, 900, 513),
 ])
 def test_attention_matches_oracle(batch, n_q, heads, n_kv, topk):
     say("attend: batch %d n_q %d heads %d n_kv %d topk %d" % (batch, n_q, heads, n_kv, topk))

@@ -5,9 +5,10 @@
 //     p_j = softmax over valid slots j of scale * q[h] . k[idx_j]
 //     o[h] = sum_j p_j v[idx_j]
 //
-// Split-K decoding: a workgroup owns one query row, 64 heads (16 per wave)
-// and one split of 256 slots, walked in chunks of 32 slots (the next
-// chunk's rows load into registers while the current one is computed).  A chunk's key
+// Split-K decoding: a workgroup owns one query row, 128 heads (16 per wave,
+// so every gathered row is loaded once for all heads) and one split of 256
+// slots, walked in chunks of 32 slots (the rows of the next two chunks load
+// into registers while the current one is computed).  A chunk's key
 // rows go to LDS (16-byte pieces, XOR-swizzled by row so the MFMA operand
 // reads are conflict free) and its value rows to a transposed LDS tile
 // (padded rows), which makes the value operand of P.V two 8-byte reads.
@@ -38,7 +39,11 @@ constexpr int kVtStride = kChunk + 8;  // bf16 per transposed value row (padded)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256, 4) void attend_split_kernel(AttnArgs a) {
+constexpr int kWaves = 8;                 // 16 heads per wave
+constexpr int kThreads = kWaves * 64;
+constexpr int kHeadsWg = kWaves * 16;
+
+__global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(AttnArgs a) {
     __shared__ __align__(16) uint8_t s_k[kChunk * kD * 2];          // swizzled key rows
     __shared__ __align__(16) __bf16 s_vt[kD * kVtStride];          // transposed value rows
     __shared__ int32_t s_valid[kChunk];
@@ -46,7 +51,7 @@ __global__ __launch_bounds__(256, 4) void attend_split_kernel(AttnArgs a) {
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t row = blockIdx.x;
     const int32_t split = blockIdx.y;
-    const int32_t head0 = blockIdx.z * 64 + wave * 16;
+    const int32_t head0 = blockIdx.z * kHeadsWg + wave * 16;
     const bool active = head0 < a.heads;
     const int32_t b = (int32_t)(row / a.n_q);
     const int32_t* idx_row = a.idx + row * a.topk;
@@ -67,43 +72,28 @@ __global__ __launch_bounds__(256, 4) void attend_split_kernel(AttnArgs a) {
     float m_run = -__builtin_inff(), l_run = 0.0f;  // of head head0 + c16
 
     const float sl2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
-    // a chunk is kChunk rows x 16 pieces for K and for V: PT + PT per thread,
-    // loaded into registers one chunk ahead of its use.  Wave w takes pieces
-    // 4w .. 4w+3 of every row, 16 rows per instruction: the transposed value
+    // A chunk is kChunk rows x 16 pieces for K and for V: one K and one V
+    // piece per thread, loaded into registers two chunks ahead of their use
+    // (two register sets).  Wave w takes pieces 4 (w % 4) .. + 3 of rows
+    // 16 (w / 4) .. + 15, 16 rows per instruction: the transposed value
     // writes then spread over 16 banks (4-way), the key writes over all.
-    constexpr int PT = kChunk / 16;  // pieces per thread and chunk
-    u32x4 kr[PT], vr4[PT];
-    bool okr[PT];
-    auto load_chunk = [&](int32_t c0) {
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int r = 16 * i + (lane & 15), c = 4 * wave + (lane >> 4);
-            const int32_t slot = c0 + r;
-            const int32_t key = slot < slot_end ? idx_row[slot] : -1;
-            okr[i] = key >= 0 && key < a.n_kv;
-            // an empty slot reads key 0 (branch-free): its score is masked,
-            // so its weight is 0 and its (finite) value row adds nothing
-            const int64_t base = ((int64_t)b * a.n_kv + (okr[i] ? key : 0)) * kD + c * 8;
-            kr[i] = *reinterpret_cast<const u32x4*>(a.k + base);
-            vr4[i] = *reinterpret_cast<const u32x4*>(a.v + base);
-        }
+    static_assert(kChunk * 16 == kThreads, "one piece per thread and chunk");
+    const int lr = 16 * (wave >> 2) + (lane & 15), lc = 4 * (wave & 3) + (lane >> 4);
+    struct Stage {
+        u32x4 k, v;
+        bool ok;
     };
-    if (slot0 < slot_end && a.n_kv > 0) load_chunk(slot0);
-    for (int32_t c0 = slot0; c0 < slot_end; c0 += kChunk) {
-        __syncthreads();  // the previous chunk's operands have been read
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int r = 16 * i + (lane & 15), c = 4 * wave + (lane >> 4);
-            *reinterpret_cast<u32x4*>(s_k + r * (kD * 2) + ((c ^ (r & 15)) * 16)) = kr[i];
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, vr4[i]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s_vt[(c * 8 + j) * kVtStride + r] = vb[j];
-            if (c == 0) s_valid[r] = okr[i] ? 1 : 0;
-        }
-        __syncthreads();
-        if (c0 + kChunk < slot_end && a.n_kv > 0) load_chunk(c0 + kChunk);  // in flight during this chunk
-        if (!active) continue;
-
+    auto load_chunk = [&](Stage& sg, int32_t c0) {
+        const int32_t slot = c0 + lr;
+        const int32_t key = slot < slot_end ? idx_row[slot] : -1;
+        sg.ok = key >= 0 && key < a.n_kv;
+        // an empty slot reads key 0 (branch-free): its score is masked,
+        // so its weight is 0 and its (finite) value row adds nothing
+        const int64_t base = ((int64_t)b * a.n_kv + (sg.ok ? key : 0)) * kD + lc * 8;
+        sg.k = *reinterpret_cast<const u32x4*>(a.k + base);
+        sg.v = *reinterpret_cast<const u32x4*>(a.v + base);
+    };
+    auto compute_chunk = [&]() {
         // S^T: keys 16 mt + 4 g + i (rows) x heads c16 (columns)
         f32x4 s[kChunk / 16];
 #pragma unroll
@@ -135,7 +125,7 @@ __global__ __launch_bounds__(256, 4) void attend_split_kernel(AttnArgs a) {
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
         // a chunk without a valid key (the same for every head) adds nothing
-        if (cmax == -__builtin_inff()) continue;
+        if (cmax == -__builtin_inff()) return;
         // the wave moves its references together (one branch for all heads)
         const bool move = cmax > m_run + 8.0f;
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
@@ -179,6 +169,29 @@ __global__ __launch_bounds__(256, 4) void attend_split_kernel(AttnArgs a) {
                 vb[4] = hi[0]; vb[5] = hi[1]; vb[6] = hi[2]; vb[7] = hi[3];
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], vb, o[dt], 0, 0, 0);
             }
+        }
+    };
+    // chunk c0 from register set sg to LDS, the set refilled with chunk
+    // c0 + 2 kChunk, then the chunk computed
+    auto step = [&](Stage& sg, int32_t c0) {
+        __syncthreads();  // the previous chunk's operands have been read
+        *reinterpret_cast<u32x4*>(s_k + lr * (kD * 2) + ((lc ^ (lr & 15)) * 16)) = sg.k;
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, sg.v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_vt[(lc * 8 + j) * kVtStride + lr] = vb[j];
+        if (lc == 0) s_valid[lr] = sg.ok ? 1 : 0;
+        __syncthreads();
+        if (c0 + 2 * kChunk < slot_end) load_chunk(sg, c0 + 2 * kChunk);  // in flight meanwhile
+        if (active) compute_chunk();
+    };
+    if (a.n_kv > 0) {
+        Stage s0, s1;
+        if (slot0 < slot_end) load_chunk(s0, slot0);
+        if (slot0 + kChunk < slot_end) load_chunk(s1, slot0 + kChunk);
+        for (int32_t c0 = slot0; c0 < slot_end; c0 += 2 * kChunk) {
+            step(s0, c0);
+            if (c0 + kChunk >= slot_end) break;
+            step(s1, c0 + kChunk);
         }
     }
     if (!active) return;
@@ -249,8 +262,8 @@ int32_t attend_splits(int32_t topk) { return (topk + kSplit - 1) / kSplit; }
 
 hipError_t launch_attend(const AttnArgs& a, int64_t rows, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
-    const dim3 g1((unsigned)rows, (unsigned)a.n_split, (unsigned)((a.heads + 63) / 64));
-    hipLaunchKernelGGL(attend_split_kernel, g1, dim3(256), 0, stream, a);
+    const dim3 g1((unsigned)rows, (unsigned)a.n_split, (unsigned)((a.heads + kHeadsWg - 1) / kHeadsWg));
+    hipLaunchKernelGGL(attend_split_kernel, g1, dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(rows * a.heads)), dim3(kD), 0, stream, a);
     return hipGetLastError();
 }

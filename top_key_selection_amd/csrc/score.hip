@@ -783,7 +783,7 @@ hipError_t launch_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream)
     const int64_t per_seq = (std::min<int64_t>(n_rows, R) + NW - 1) / NW;
     // segments: a multiple of the stage, sized for a few workgroups per CU
     const int64_t want = n_rows * (int64_t)a.n_cols / (NW * 2048);
-    int64_t seg = std::min<int64_t>(4096, std::max<int64_t>(512, (want + 63) / 64 * 64));
+    int64_t seg = std::min<int64_t>(4096, std::max<int64_t>(512, (want + 127) / 128 * 128));
     while ((a.n_cols + seg - 1) / seg > 65535) seg *= 2;
     dim3 grid((unsigned)(n_seq * per_seq), (unsigned)((a.n_cols + seg - 1) / seg));
     hipLaunchKernelGGL((score_shared_kernel<MB, NW>), grid, dim3(NW * 64), 0, stream, a, n_rows,
