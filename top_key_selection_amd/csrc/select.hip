@@ -1425,13 +1425,16 @@ void launch_nt(const SelectArgs& a, int64_t n_rows, dim3 grid, hipStream_t strea
 
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0) return hipSuccess;
-    // few rows: a wide workgroup per row; many rows: three 512-thread ones
-    // per CU (the LDS holds three), so that one row's sampling and final
-    // sort overlap the others' streaming passes
+    // few rows: a wide workgroup per row; many long rows: three 512-thread
+    // ones per CU (the LDS holds three), so that one row's sampling and
+    // final sort overlap the others' streaming passes; many short rows
+    // (block lists): 256 threads, whose barriers cost less
     if (n_rows < 512)
         launch_nt<1024>(a, n_rows, dim3((unsigned)n_rows), stream);
-    else
+    else if (a.n_cols > 2048)
         launch_nt<512>(a, n_rows, dim3((unsigned)n_rows), stream);
+    else
+        launch_nt<256>(a, n_rows, dim3((unsigned)n_rows), stream);
     return hipGetLastError();
 }
 
