@@ -1425,10 +1425,11 @@ void launch_nt(const SelectArgs& a, int64_t n_rows, dim3 grid, hipStream_t strea
 
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0) return hipSuccess;
-    // few rows: a wide workgroup per row; many long rows: three 512-thread
-    // ones per CU (the LDS holds three), so that one row's sampling and
-    // final sort overlap the others' streaming passes; many short rows
-    // (block lists): 256 threads, whose barriers cost less
+    // few rows: a wide workgroup per row; many long rows: 512-thread ones
+    // (two per CU at 95 VGPRs), which keep more loads in flight per row and
+    // let one row's sampling and final sort overlap the other's streaming
+    // pass; many short rows (block lists): 256 threads, whose barriers cost
+    // less
     if (n_rows < 512)
         launch_nt<1024>(a, n_rows, dim3((unsigned)n_rows), stream);
     else if (a.n_cols > 2048)
