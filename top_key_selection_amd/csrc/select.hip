@@ -12,7 +12,8 @@
 // the candidates arrive in.  A row takes one of three routes:
 //
 //   * at most 2048 candidates: all of them are gathered into LDS and sorted;
-//   * at least 16384 candidates: a threshold from a small sample of the row
+//   * at least 4096 candidates (16384 for kept-block rows): a threshold
+//     from a small sample of the row
 //     (the Indexer-TopK abstract on the StreamIndex page: estimate the score
 //     range from a sample, keep only candidates above a tight threshold,
 //     stay exact) fills an LDS pool in one pass;
@@ -50,6 +51,7 @@ constexpr int kSamples = 2048;      // candidates sampled for the prefilter thre
 constexpr int kSampleRun = 16;      // ... in evenly spaced runs of consecutive candidates
 static_assert(kSamples % 256 == 0 && kSamples % 1024 == 0, "whole samples per thread");
 constexpr int kPrefilterMin = 16384; // rows at least this long take the prefilter
+constexpr int kPrefilterMinTok = 4096; // ... token rows (not block lists) from this long
 constexpr int kMaxBlkEntries = 512;
 constexpr int kBitmapWords = 4096;  // block-select bitmap (ids below 131072)
 
@@ -1244,7 +1246,10 @@ __device__ __forceinline__ int32_t select_core(const SelectArgs& a, const RowCtx
         sorted = true;
         return min(K, n);
     }
-    if (n_total > K && n_total < kPrefilterMin) return select_hist<VEC, NT>(a, r, L, K, sorted);
+    // (the refinement rows of kept blocks keep the histogram route below
+    // 16384: there the sampled threshold was measured slower)
+    if (n_total > K && n_total < (a.blocks_mode ? kPrefilterMin : kPrefilterMinTok))
+        return select_hist<VEC, NT>(a, r, L, K, sorted);
     if (n_total > kCap) {
         if (!sample_threshold<NT>(a, r, L, n_total, K, tau)) return select_hist<VEC, NT>(a, r, L, K, sorted);
     }
