@@ -413,6 +413,30 @@ def test_topk_scores_threshold_prefilter_cases():
             np.testing.assert_array_equal(gv[r][ok], sc[r][want[ok]] + np.float32(0.0))
 
 
+@pytest.mark.parametrize("R", [8, 520])
+@pytest.mark.parametrize("n_cols", [2049, 4095, 4096, 4097, 8192, 16383, 16384])
+def test_topk_scores_route_boundaries(R, n_cols):
+    """Row lengths on both sides of every route boundary (gather-and-sort up
+    to 2048, histogram below 4096, sampled threshold from 4096 token
+    candidates, the few-row and many-row workgroup sizes), integer scores
+    with heavy ties and float rows, against a full sort."""
+    say("topk_scores route boundaries R=%d n=%d" % (R, n_cols))
+    rng = np.random.default_rng(R * 100000 + n_cols)
+    sc = rng.integers(-6, 7, (R, n_cols)).astype(np.float32)
+    sc[1::3] = rng.standard_normal((len(range(1, R, 3)), n_cols)).astype(np.float32)
+    sc[2, :] = 1.0                                           # one tie group
+    idx_all = np.broadcast_to(np.arange(n_cols), sc.shape)
+    order = np.lexsort((idx_all, -sc.astype(np.float64)), axis=-1)
+    for topk in (2048, 700):
+        idx, vals = tks.topk_scores(dev(sc), topk)
+        torch.cuda.synchronize()
+        gi, gv = host(idx), host(vals)
+        want = order[:, :topk]
+        bad = np.nonzero((gi != want).any(axis=1))[0]
+        assert len(bad) == 0, "k=%d: %d rows differ, first %d" % (topk, len(bad), bad[0])
+        np.testing.assert_array_equal(gv, np.take_along_axis(sc, want, axis=1) + np.float32(0.0))
+
+
 def test_tiled_rows_with_prior_list_take_the_prefilter_exactly():
     """Key tiles longer than the LDS pool plus the running list of earlier
     tiles: the sampled threshold covers both, integer scores (many ties)."""
