@@ -330,7 +330,10 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     using RG = Fp8Ring<D>;
     constexpr int KS = D / 16;
     __shared__ __align__(16) uint8_t ring[4 * RG::WAVE];
-    __shared__ __align__(16) uint16_t s_q[MB * 32 * D];  // the row's q, zero-padded heads
+    // the row's q, zero-padded heads; rows padded by 16 bytes so that the
+    // fragment reads (32 head rows, one column) spread over the banks
+    constexpr int QS = D + 8;
+    __shared__ __align__(16) uint16_t s_q[MB * 32 * QS];
     __shared__ float s_w[MB * 32];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
         for (int e = threadIdx.x * 8; e < MB * 32 * D; e += 256 * 8) {
             u32x4 v = u32x4{0, 0, 0, 0};
             if (e < hq) v = *reinterpret_cast<const u32x4*>(qsrc + e);
-            *reinterpret_cast<u32x4*>(&s_q[e]) = v;
+            *reinterpret_cast<u32x4*>(&s_q[(e / D) * QS + e % D]) = v;
         }
         for (int h = threadIdx.x; h < MB * 32; h += 256) s_w[h] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
     }
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qa[mb][ks] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(&s_q[h * D + hf * (D / 2) + ks * 8]));
+                bf16x8, *reinterpret_cast<const u32x4*>(&s_q[h * QS + hf * (D / 2) + ks * 8]));
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
