@@ -111,7 +111,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
+              "(query rows would shard across GPUs with no exchange between them). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
