@@ -110,7 +110,7 @@ def pmc_traffic(role, workload, src_files):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(query rows would shard across GPUs with no exchange between them). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
