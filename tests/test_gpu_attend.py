@@ -99,3 +99,22 @@ def test_attention_decode_full_size():
         vf = host(v[b:b + 1].float())
         ref = oracle.sparse_attention(qf, kf, vf, idx[b:b + 1], scale)
         check(host(out[b:b + 1]), ref, np.abs(vf[0, idx[b, 0]]).max(), "row %d" % b)
+
+
+def test_attention_into_a_4_byte_aligned_output():
+    """The output need only be 4-byte aligned: a buffer one float past a
+    16-byte boundary gives the same values as an aligned one."""
+    say("attend into an output offset by one float")
+    g = torch.Generator(device="cuda").manual_seed(9)
+    B, T, H, n, K = 2, 2, 64, 500, 300
+    q = torch.randn((B, T, H, 128), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn((B, n, 128), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((B, n, 128), device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.randint(-1, n, (B, T, K), device="cuda", generator=g, dtype=torch.int32)
+    ref = tks.sparse_attention(q, k, v, idx, 0.09)
+    buf = torch.full((B * T * H * 128 + 1,), 7.0, device="cuda")
+    out = buf[1:].view(B, T, H, 128)
+    assert out.data_ptr() % 16 == 4
+    tks.sparse_attention(q, k, v, idx, 0.09, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and buf[0].item() == 7.0

@@ -212,42 +212,57 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(AttnArgs a) {
 }
 
 // o = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s with m the largest
-// running max; zeros for a row without a valid key.  Every split's
+// running max; zeros for a row without a valid key.  A workgroup merges
+// four (row, head) pairs, 32 threads each with four dims; every split's
 // partial is loaded before any is used (n_split <= kMaxSplits).
 constexpr int kMaxSplits = 2048 / kSplit;
+constexpr int kMergeHeads = 4;
 
-__global__ __launch_bounds__(128) void attend_merge_kernel(AttnArgs a) {
-    const int64_t rh = blockIdx.x;  // row * heads + h
-    const int d = threadIdx.x;
+__global__ __launch_bounds__(128) void attend_merge_kernel(AttnArgs a, int64_t n_rh) {
+    const int64_t rh = (int64_t)blockIdx.x * kMergeHeads + (threadIdx.x >> 5);  // row * heads + h
+    if (rh >= n_rh) return;
+    const int d = (threadIdx.x & 31) * 4;
     const int64_t row = rh / a.heads;
     const int h = (int)(rh % a.heads);
-    float ms[kMaxSplits], ls[kMaxSplits], os[kMaxSplits];
+    float ms[kMaxSplits], ls[kMaxSplits];
+    f32x4 os[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
         ms[s] = -__builtin_inff();
         ls[s] = 0.0f;
-        os[s] = 0.0f;
+        os[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (s < a.n_split) {
             const int64_t p = (row * a.n_split + s) * a.heads + h;
             ms[s] = a.ml_part[p * 2];
             ls[s] = a.ml_part[p * 2 + 1];
-            os[s] = a.o_part[p * kD + d];
+            os[s] = *reinterpret_cast<const f32x4*>(a.o_part + p * kD + d);
         }
     }
     float m = -__builtin_inff();
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) m = fmaxf(m, ms[s]);
-    float acc = 0.0f, l = 0.0f;
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float l = 0.0f;
     if (m != -__builtin_inff()) {
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
             if (ms[s] == -__builtin_inff()) continue;
             const float f = exp2f(ms[s] - m);
             l += f * ls[s];
-            acc += f * os[s];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += f * os[s][i];
         }
     }
-    a.out[rh * kD + d] = l > 0.0f ? acc / l : 0.0f;
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = l > 0.0f ? acc[i] / l : 0.0f;
+    float* op = a.out + rh * kD + d;
+    if ((reinterpret_cast<uintptr_t>(a.out) & 15u) == 0) {
+        *reinterpret_cast<f32x4*>(op) = o;
+    } else {  // out need only be 4-byte aligned
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[i] = o[i];
+    }
 }
 
 }  // namespace
@@ -264,7 +279,8 @@ hipError_t launch_attend(const AttnArgs& a, int64_t rows, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     const dim3 g1((unsigned)rows, (unsigned)a.n_split, (unsigned)((a.heads + kHeadsWg - 1) / kHeadsWg));
     hipLaunchKernelGGL(attend_split_kernel, g1, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(rows * a.heads)), dim3(kD), 0, stream, a);
+    hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)((rows * a.heads + kMergeHeads - 1) / kMergeHeads)),
+                       dim3(128), 0, stream, a, rows * (int64_t)a.heads);
     return hipGetLastError();
 }
 
