@@ -39,8 +39,10 @@ def brute_topk(scores, valid, k):
 def test_bf16_decode_matches_torch_for_all_patterns():
     bits = np.arange(65536, dtype=np.uint16)
     ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
-    got = np.array([oracle.bf16_to_double(int(b)) for b in bits[::7]])
-    np.testing.assert_array_equal(got, ref[::7])
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.isnan(got[nan]).all()
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
 
 
 def test_e4m3fn_decode_matches_torch_for_all_codes():
@@ -93,6 +95,90 @@ def test_single_head_unit_weight_is_relu_of_matmul():
     causal = np.tril(np.ones((T, T), bool))
     np.testing.assert_array_equal(got[causal], ref[causal])
     assert np.all(np.isneginf(got[~causal]))
+
+
+def _torch_decode_keys(k, fp8, k_scale):
+    """Keys as float64 through torch's own casts (independent of the oracle's
+    decoders); fp8 keys are scale * e4m3fn."""
+    if fp8:
+        v = torch.from_numpy(k).view(torch.float8_e4m3fn).double().numpy()
+        return v * k_scale.astype(np.float64)[..., None]
+    return torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _definition_scores(q_rows, w_rows, kd, rows, n_q, q_pos0, ratio):
+    """I[t,s] = sum_h w[t,h] * max(0, q[t,h] . k[s]) from a numpy matmul,
+    -inf where s > floor((q_pos0 + t) / ratio) (Python floor division)."""
+    qd = torch.from_numpy(q_rows.view(np.int16)).view(torch.bfloat16).double().numpy()
+    n_k = kd.shape[1]
+    out = np.empty((len(rows), n_k))
+    for i, r in enumerate(rows):
+        b, t = divmod(int(r), n_q)
+        x = qd[i] @ kd[b].T                       # [H, n_k]
+        out[i] = w_rows[i].astype(np.float64) @ np.maximum(x, 0.0)
+        vis = (q_pos0 + t) // ratio
+        out[i, np.arange(n_k) > vis] = -np.inf
+    return out
+
+
+@pytest.mark.parametrize("fp8", [0, 1])
+@pytest.mark.parametrize("q_pos0,ratio", [(0, 1), (-3, 4), (5, 4), (-9, 3)])
+def test_row_scores_equal_the_definition_on_integer_inputs(fp8, q_pos0, ratio):
+    """row_scores (the score every float comparator uses) against the
+    definition written with torch's decoders and a numpy matmul: batch 2,
+    compressed causality, negative q_pos0, bf16 and fp8 keys.  Integer
+    inputs and power-of-two scales keep every score exact in float64, so the
+    two must agree bit for bit, -inf included."""
+    rng = np.random.default_rng(40 + fp8 + 2 * ratio)
+    B, T, NK, H, D = 2, 37, 29, 3, 16
+    q = rand_int(rng, (B, T, H, D))
+    w = rand_int(rng, (B, T, H))
+    kv = rand_int(rng, (B, NK, D))
+    if fp8:
+        k = fp32_to_e4m3fn(kv)
+        ks = (2.0 ** rng.integers(-3, 4, (B, NK))).astype(np.float32)
+    else:
+        k, ks = fp32_to_bf16_bits(kv), None
+    S = shp(T, NK, H, D, batch=B, q_pos0=q_pos0, ratio=ratio, fp8=fp8)
+    rows = np.array([0, 1, 5, T - 1, T, T + 7, 2 * T - 1])
+    qb = fp32_to_bf16_bits(q).reshape(B * T, H, D)[rows]
+    wr = w.reshape(B * T, H)[rows]
+    got = oracle.row_scores(S, qb, wr, k, ks, rows)
+    ref = _definition_scores(qb, wr, _torch_decode_keys(k, fp8, ks), rows, T, q_pos0, ratio)
+    np.testing.assert_array_equal(got, ref)
+    # the same scores as the rectangle form, row for row
+    rect = oracle.index_scores(S, fp32_to_bf16_bits(q), w, k, ks, 0, T, 0, NK)
+    np.testing.assert_array_equal(got, rect.reshape(B * T, NK)[rows])
+
+
+@pytest.mark.parametrize("fp8", [0, 1])
+def test_row_scores_on_float_inputs_match_the_definition_and_the_topk_values(fp8):
+    """Float inputs: row_scores within float64 rounding of the torch/numpy
+    definition, -inf exactly outside the causal prefix, and equal to the
+    values orc_topk_flat reports at the indices it selects."""
+    rng = np.random.default_rng(50 + fp8)
+    B, T, NK, H, D, K = 2, 64, 300, 8, 32, 40
+    q = fp32_to_bf16_bits(rng.standard_normal((B, T, H, D)).astype(np.float32))
+    w = (rng.standard_normal((B, T, H)) / np.sqrt(H)).astype(np.float32)
+    z = rng.standard_normal((B, NK, D)).astype(np.float32)
+    if fp8:
+        ks = (np.abs(z).max(axis=2) / 448.0).astype(np.float32)
+        k = fp32_to_e4m3fn(z / ks[..., None])
+    else:
+        k, ks = fp32_to_bf16_bits(z), None
+    q_pos0 = NK - T - 10
+    S = shp(T, NK, H, D, batch=B, q_pos0=q_pos0, fp8=fp8)
+    rows = np.arange(B * T)
+    qr, wr = q.reshape(B * T, H, D), w.reshape(B * T, H)
+    got = oracle.row_scores(S, qr, wr, k, ks, rows)
+    ref = _definition_scores(qr, wr, _torch_decode_keys(k, fp8, ks), rows, T, q_pos0, 1)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got))
+    scale = np.abs(ref[fin]).max()
+    assert np.max(np.abs(got[fin] - ref[fin])) <= 1e-12 * scale
+    idx, val = oracle.topk_flat(S, qr, wr, k, ks, K, rows)
+    ok = idx >= 0
+    np.testing.assert_array_equal(val[ok], got[np.nonzero(ok)[0], idx[ok]])
 
 
 def test_basis_keys_pick_one_coordinate_per_head():
