@@ -9,8 +9,11 @@
  *   scans every visible key; the HISA form mean-pools keys into blocks,
  *   scores the pooled representatives, keeps the best blocks and runs the
  *   same token indexer only inside them.  Both emit the same per-query top-k
- *   index set.  Selection is streamed over query chunks and key tiles with a
- *   partition-merge of partial top-k lists, so no [queries x keys] score
+ *   index set.  Selection is streamed: either over query chunks and key
+ *   tiles with a partition-merge of partial top-k lists (a tile never holds
+ *   every row's scores of every visible key), or, for one query per
+ *   sequence, fused into the scoring pass so that only the promising
+ *   candidates of each key segment are written.  No [queries x keys] score
  *   tensor is ever allocated.
  *
  * Conventions shared by every call:
@@ -104,7 +107,19 @@ int tks_indexer_scores(const tks_shape* shape, const void* q, const float* w, co
  * partition-merge top-k).  Query rows are processed in chunks of q_chunk
  * rows; keys in tiles of k_tile keys; each tile's partial top-k is merged
  * into a running per-row list.  q_chunk = 0 / k_tile = 0 pick sizes
- * automatically.  The result does not depend on q_chunk or k_tile.
+ * automatically, and the automatic tile never covers every row and every
+ * visible key.
+ * With one query per sequence (n_q = 1, decode), dim 128 and both sizes
+ * automatic, scoring and selection are fused instead (StreamIndex
+ * abstract; the threshold-based Indexer-TopK abstract on the same page:
+ * write back only the promising candidates and stay exact): each
+ * 4096-key segment keeps its best candidates above a threshold of its
+ * own, a finish pass selects the row's top-k from them and proves the
+ * result exact (its k-th best is at least every segment's threshold),
+ * and a row that fails the proof (heavily tied or clustered scores) is
+ * rescored and selected exactly.  The workspace then holds at most 4096
+ * candidates per row, not the row's scores.
+ * The result does not depend on q_chunk, k_tile or the form taken.
  *   idx:  int32 [batch, n_q, topk];  vals: fp32 [batch, n_q, topk] or NULL.
  * The workspace size depends only on (shape, topk, q_chunk, k_tile).
  */
@@ -114,6 +129,15 @@ int tks_topk_flat(const tks_shape* shape, const void* q, const float* w, const v
                   const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
                   int32_t* idx, float* vals, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * Diagnostic of the fused form: *n_redone (host pointer) receives how many
+ * rows of the last tks_topk_flat call that used `workspace` with the same
+ * (shape, topk, q_chunk, k_tile) took the exact rescoring path; 0 for the
+ * tiled form.  Waits for `stream`.
+ */
+int tks_topk_flat_redone(const tks_shape* shape, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                         const void* workspace, int32_t* n_redone, hipStream_t stream);
 
 /*
  * Top-k of rows of a score matrix that is already in device memory (the

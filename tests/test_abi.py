@@ -94,6 +94,32 @@ def test_workspace_queries():
     assert tks.topk_flat_workspace(tks.Shape(1, 8, 8, 0, 32), 4) == 0   # invalid -> 0
 
 
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_no_workload_plan_holds_every_score(cid):
+    """The automatic flat plan of every workload stays below the fp32
+    [batch * n_q, n_k] score tensor (StreamIndex abstract: the chunked
+    partition-merge never materialises the full intermediate)."""
+    from tks_inputs import CONFIGS
+    cfg = CONFIGS[cid]
+    s = tks.Shape(**cfg.shape_dict())
+    full = cfg.batch * cfg.n_q * cfg.n_k * 4
+    for qc, kt in {(0, 0), (cfg.q_chunk, cfg.k_tile)}:
+        ws = tks.topk_flat_workspace(s, cfg.topk, qc, kt)
+        assert 0 < ws < full, (cid, qc, kt, ws, full)
+
+
+def test_fused_decode_plan_holds_survivors_not_scores():
+    """One query per sequence: the fused plan keeps at most 4096 candidates
+    per row (8-byte composites) and a bounded rescoring arena; the decode
+    workload's 64 x 65,536 scores (16 MiB) are never held."""
+    s = tks.Shape(64, 1, 65536, 64, 128, q_pos0=65535, key_dtype=tks.KEY_FP8_E4M3FN)
+    ws = tks.topk_flat_workspace(s, 2048)
+    assert ws <= 64 * 4096 * 8 + 64 * (4096 + 2 * 2048) * 4 + 64 * 1024
+    assert ws < 64 * 65536 * 4 // 3
+    # explicit chunk / tile sizes keep the tiled partition-merge
+    assert tks.topk_flat_workspace(s, 2048, 64, 16384) == 64 * 16384 * 4 + 2 * 64 * 2048 * 4
+
+
 def test_materialized_score_size_matches_pages():
     # StreamIndex abstract: [B,S,H_I,T] fp32 at S=65,536, H_I=64, T=S/4 is 256 GB
     assert tks.materialized_score_bytes(1, 65536, 64, 65536 // 4) == 2 ** 38

@@ -143,7 +143,9 @@ def test_hisa_vs_flat_prefill_32k_full_size():
     x, kd = upload(cfg)
     S = tks.Shape(**cfg.shape_dict())
     gi, gv = run_flat(cfg, S, *kd)
-    rows = sample_rows(cfg, 48)
+    # 256 rows: first / last, around topk - 1, around the 128-key block
+    # boundaries and the 8192-row chunk boundaries, the rest uniform
+    rows = sample_rows(cfg, 256, extra=[8191, 8192, 16383, 16384, 24575, 24576])
     flat_check(cfg, x, gi, gv, rows, "flat 32k")
     pooled, blk, hi, hv = run_hisa(cfg, S, *kd)
     hisa_check(cfg, x, pooled, blk, hi, hv, rows, "hisa 32k", kd)
@@ -160,10 +162,10 @@ def test_decode_64k_fp8_full_size():
     x, kd = upload(cfg)
     S = tks.Shape(**cfg.shape_dict())
     gi, gv = run_flat(cfg, S, *kd)
-    rows = np.array([0, 1, 17, 31, 32, 50, 62, 63])
+    rows = np.arange(cfg.rows)  # every sequence
     flat_check(cfg, x, gi, gv, rows, "flat decode")
     pooled, blk, hi, hv = run_hisa(cfg, S, *kd)
-    hisa_check(cfg, x, pooled, blk, hi, hv, np.arange(0, 64, 4), "hisa decode", kd)
+    hisa_check(cfg, x, pooled, blk, hi, hv, rows, "hisa decode", kd)
     u = iou(hi, gi)
     print("HISA vs flat IoU (i.i.d. keys): mean %.4f" % u.mean())
 
@@ -188,5 +190,10 @@ def test_streaming_256k_compressed_full_size():
           "would be %.0f GiB" % (working / 2 ** 20,
                                  tks.materialized_score_bytes(1, cfg.n_q, 1, cfg.n_k) / 2 ** 30))
     assert working < 512 * 2 ** 20
-    rows = sample_rows(cfg, 40)
+    # 256 rows, including the rows around every 8192-key tile boundary (a
+    # query at row t sees compressed keys up to floor(t / 4)) and the
+    # 4096-row chunk boundaries
+    tile_rows = [cfg.causal_ratio * cfg.k_tile * j + d for j in range(1, cfg.n_k // cfg.k_tile)
+                 for d in (-1, 0, cfg.causal_ratio - 1, cfg.causal_ratio)]
+    rows = sample_rows(cfg, 256, extra=tile_rows)
     flat_check(cfg, dict(q=None, w=None, k=k, k_scale=None), gi, gv, rows, "stream 256k")

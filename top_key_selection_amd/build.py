@@ -1,22 +1,29 @@
 """Build libtks.so (the gfx950 kernels + C ABI) in-tree with hipcc.
 
     python -m top_key_selection_amd.build
+
+Each source is compiled to its own object (in parallel; every kernel is
+launched from the file that defines it, so no relocatable device code is
+needed), then the objects are linked into one shared library.
 """
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtks.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "pool.hip", "append.hip", "gather.hip", "attend.hip"]
+OBJ = os.path.join(ROOT, "_build", "tks")
+SOURCES = ["api.hip", "score.hip", "fused.hip", "select.hip", "pool.hip", "append.hip",
+           "gather.hip", "attend.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-command-line-argument",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -24,19 +31,33 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; drop that note
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
+    return r.returncode, out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    objs = [os.path.join(OBJ, s.replace(".hip", ".o")) for s in srcs]
+    cmds = [[HIPCC] + FLAGS + ["-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        res = list(ex.map(_run, cmds))
+    for (rc, out), s in zip(res, srcs):
+        if rc != 0:
+            raise RuntimeError("hipcc failed on %s:\n%s" % (s, out))
+        if verbose and out.strip():
+            print(out)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp])
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + out)
     os.replace(tmp, LIB)
     return LIB
 

@@ -134,20 +134,55 @@ int block_shift_of(int32_t block) {
 }
 
 // ------------------------------------------------------------- flat planning
+//
+// Two forms, neither of which holds the scores of every row and key:
+//   * fused (one query per sequence, D = 128, chunk and tile left to the
+//     library): segments of kFusedSeg keys are scored and filtered in one
+//     pass; the workspace holds at most kFusedPoolCap survivors per row plus
+//     the rescoring arena of the exact fallback;
+//   * tiled: a [q_chunk, k_tile] fp32 score tile and the running top-k lists
+//     of a chunk; the automatic sizes stay within kScoreBudget and never let
+//     one tile cover every row and every visible key.
+
+constexpr int32_t kFusedMaxSeg = 256;
 
 struct FlatPlan {
+    bool fused;
     int64_t rows;
     int32_t q_chunk;
     int32_t k_tile;
     int64_t score_stride;
     tks::SelectSplit split;  // few long rows over every CU (single tile only)
-    size_t off_scores, off_run_val, off_run_idx, off_split, bytes;
+    size_t off_scores, off_run_val, off_run_idx, off_split;
+    int32_t n_seg, r_cap;    // fused
+    size_t off_cand, off_count, off_tau, off_failed, off_arena;
+    size_t bytes;
 };
 
 FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile) {
     FlatPlan p{};
     p.rows = (int64_t)s->batch * s->n_q;
     const int32_t maxvis = p.rows > 0 ? max_visible(s, 0, p.rows) : 0;
+    const int64_t n_seg = ((int64_t)maxvis + tks::kFusedSeg - 1) / tks::kFusedSeg;
+    if (q_chunk == 0 && k_tile == 0 && s->n_q == 1 && s->dim == 128 && n_seg >= 1 &&
+        n_seg <= kFusedMaxSeg) {
+        p.fused = true;
+        p.n_seg = (int32_t)n_seg;
+        p.r_cap = std::min<int32_t>(tks::kFusedSeg, tks::kFusedPoolCap / p.n_seg);
+        size_t off = 0;
+        p.off_cand = off;
+        off += round_up(p.rows * n_seg * p.r_cap * 8, 256);
+        p.off_count = off;
+        off += round_up(p.rows * n_seg * 4, 256);
+        p.off_tau = off;
+        off += round_up(p.rows * n_seg * 4, 256);
+        p.off_failed = off;  // failed-row list, then its counter
+        off += round_up((p.rows + 1) * 4, 256);
+        p.off_arena = off;
+        off += round_up((int64_t)tks::fused_arena_bytes(p.rows, topk), 256);
+        p.bytes = off;
+        return p;
+    }
     int64_t kt = k_tile > 0 ? k_tile : round_up(std::max<int32_t>(maxvis, 1), 32);
     int64_t qc;
     if (q_chunk > 0) {
@@ -157,6 +192,14 @@ FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_
         if (k_tile <= 0 && qc < std::min<int64_t>(p.rows, 1024)) {
             kt = 16384;
             qc = std::max<int64_t>(1, kScoreBudget / (kt * 4));
+        }
+        // one tile would hold every row's scores of every visible key:
+        // split the rows into four chunks (a single row: two key tiles)
+        if (qc >= p.rows && kt >= maxvis) {
+            if (p.rows > 1)
+                qc = (p.rows + 3) / 4;
+            else if (k_tile <= 0 && maxvis > 32)
+                kt = round_up((maxvis + 1) / 2, 32);
         }
     }
     qc = std::max<int64_t>(1, std::min<int64_t>(qc, std::max<int64_t>(p.rows, 1)));
@@ -253,6 +296,58 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
     if (!aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
 
     char* ws = static_cast<char*>(workspace);
+    if (p.fused) {
+        const bool fp8k = s->key_dtype == TKS_KEY_FP8_E4M3FN;
+        const tks::FusedPool pool{reinterpret_cast<uint64_t*>(ws + p.off_cand),
+                                  reinterpret_cast<int32_t*>(ws + p.off_count),
+                                  reinterpret_cast<uint32_t*>(ws + p.off_tau), p.n_seg, p.r_cap};
+        const tks::RowMap rm{0, s->n_q, 0, s->n_q};
+        tks::ScoreArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.w = w;
+        a.k = k;
+        a.k_scale = k_scale;
+        a.k_seq_len = s->n_k;
+        a.heads = s->heads;
+        a.rows = rm;
+        a.vis = vis_tokens(s);
+        a.col_key0 = 0;
+        a.n_cols = p.n_seg * tks::kFusedSeg;
+        a.stream_keys = 1;
+        a.fuse = pool;
+        a.fuse_clear = reinterpret_cast<int32_t*>(ws + p.off_failed) + rows;
+        hipError_t e;
+        {
+            Timed tm("score_flat", stream);
+            e = tks::launch_score_fused(a, rows, p.n_seg, fp8k, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "fused score launch");
+        tks::FusedFinishArgs f{};
+        f.pool = pool;
+        f.sel.rows = rm;
+        f.sel.vis = vis_tokens(s);
+        f.sel.topk = topk;
+        f.sel.out_val = vals;
+        f.sel.out_idx = idx;
+        f.sel.out_width = topk;
+        f.sel.always_final = 1;
+        f.q = static_cast<const uint16_t*>(q);
+        f.w = w;
+        f.k = k;
+        f.k_scale = k_scale;
+        f.k_seq_len = s->n_k;
+        f.heads = s->heads;
+        f.arena = reinterpret_cast<float*>(ws + p.off_arena);
+        f.failed = reinterpret_cast<int32_t*>(ws + p.off_failed);
+        f.n_failed = f.failed + rows;
+        f.n_rows = rows;
+        {
+            Timed tm("select_flat", stream);
+            e = tks::launch_fused_finish(f, fp8k, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "fused finish launch");
+        return TKS_OK;
+    }
     float* sbuf = reinterpret_cast<float*>(ws + p.off_scores);
     float* run_val = reinterpret_cast<float*>(ws + p.off_run_val);
     int32_t* run_idx = reinterpret_cast<int32_t*>(ws + p.off_run_idx);
@@ -315,6 +410,23 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
             if (e != hipSuccess) return hip_fail(e, "select launch");
         }
     }
+    return TKS_OK;
+}
+
+int tks_topk_flat_redone(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                         const void* workspace, int32_t* n_redone, hipStream_t stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (topk < 1 || topk > kMaxTopk || q_chunk < 0 || k_tile < 0 || !n_redone)
+        return fail(TKS_EINVAL, "bad topk / q_chunk / k_tile, or n_redone is NULL");
+    const FlatPlan p = plan_flat(s, topk, q_chunk, k_tile);
+    *n_redone = 0;
+    if (!p.fused) return TKS_OK;
+    if (!workspace) return fail(TKS_EINVAL, "workspace is NULL");
+    const char* cnt = static_cast<const char*>(workspace) + p.off_failed + p.rows * 4;
+    hipError_t e = hipMemcpyAsync(n_redone, cnt, 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "reading the redone-row count");
     return TKS_OK;
 }
 

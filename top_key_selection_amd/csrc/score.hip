@@ -20,76 +20,178 @@
 //     to the reduced score (scale >= 0 commutes with the ReLU).
 #include <algorithm>
 
-#include "tks_launch.hpp"
+#include "score_common.hpp"
 
 namespace tks {
 
 namespace {
 
-template <int D, bool FP8>
-struct KeyFrag {
-    // bf16: D/2 bf16 = D bytes per lane; fp8: D/2 bytes per lane.
-    static constexpr int kBytes = FP8 ? D / 2 : D;
-    static constexpr int kVec = kBytes / 16;
-    u32x4 v[kVec];
-};
-
-// Branch-free fragment load (the caller clamps `row` into the key tensor for
-// slots that hold no key), so the compiler can keep several loads in
-// flight and wait for each one by count.
-template <int D, bool FP8>
-__device__ inline void load_key(KeyFrag<D, FP8>& f, const void* k, int64_t row, int hf) {
-    constexpr int KB = KeyFrag<D, FP8>::kBytes;
-    const u32x4* p = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const uint8_t*>(k) + row * (int64_t)(FP8 ? D : 2 * D) + hf * KB);
-#pragma unroll
-    for (int i = 0; i < KeyFrag<D, FP8>::kVec; ++i) f.v[i] = p[i];
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // Block-list entries of one row (HISA kept blocks, forced ones included).
 constexpr int kMaxBlkEntries = 512;
 
-// max(0, x) in one integer max on the bit pattern: negative floats (and -0)
-// are negative integers, non-negative floats keep their order.  Inputs are
-// finite, so no NaN handling is needed.
-__device__ __forceinline__ float relu_bits(float x) {
-    return __int_as_float(max(__float_as_int(x), 0));
+
+// ------------------------------------------------------------------------
+// Fused segment filter.  A workgroup that scored one segment of a row holds
+// the segment's score keys in LDS (key 0: no candidate).  It keeps at most
+// r_cap of them without sorting: the keep threshold T is the smallest key
+// value that at most r_cap keys reach, found by two rounds of a 1024-bin
+// histogram over the key range [kmin, kmax] (the second round inside the
+// first round's boundary bin; when that bin is wider than one key value the
+// whole boundary sub-bin is dropped, which keeps fewer, never more).  Keys
+// at or above T leave as composites (score key << 32 | ~index), and T goes
+// with them: every dropped key of the segment is below T.
+
+constexpr int kFilterBins = 1024;
+constexpr int kFilterScratch = kFilterBins + 32;  // words: bins, wave sums, results
+
+__device__ __forceinline__ uint64_t fz_composite(uint32_t key, int32_t idx) {
+    return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-// B operand of k-step ks from a key fragment.
-template <int D, bool FP8>
-__device__ inline bf16x8 key_operand(const KeyFrag<D, FP8>& f, int ks) {
-    if constexpr (!FP8) {
-        return __builtin_bit_cast(bf16x8, f.v[ks]);
-    } else {
-        // 8 fp8 codes = 2 dwords of vector ks/2
-        const u32x4& v = f.v[ks >> 1];
-        uint32_t d0 = (ks & 1) ? v[2] : v[0];
-        uint32_t d1 = (ks & 1) ? v[3] : v[1];
-        bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, false);
-        bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, true);
-        bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, false);
-        bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, true);
-        bf16x8 r;
-        r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-        r[4] = c[0]; r[5] = c[1]; r[6] = e[0]; r[7] = e[1];
-        return r;
+// Bin of hist[0, NB) holding the R-th largest entry (1-based; the total is
+// at least R): res[0] = bin, res[1] = entries in the bins above it.
+template <int NT>
+__device__ __forceinline__ void fz_rank_bin(const uint32_t* hist, int32_t R, int32_t* wsum,
+                                            uint32_t* res) {
+    constexpr int NB = kFilterBins, PER = NB / NT, NW = NT / 64;
+    static_assert(PER * NT == NB, "bins per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t c[PER];
+    int32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        c[i] = (int32_t)hist[NB - 1 - (PER * tid + i)];  // descending bins
+        sum += c[i];
+    }
+    int32_t inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) inc += w < wave ? wsum[w] : 0;
+    int32_t cum = inc - sum;
+    if (cum < R && R <= inc) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (cum < R && R <= cum + c[i]) {
+                res[0] = (uint32_t)(NB - 1 - (PER * tid + i));
+                res[1] = (uint32_t)cum;
+            }
+            cum += c[i];
+        }
+    }
+    __syncthreads();
+}
+
+// Filter stash[0, n) (n_valid valid keys) of segment `seg` of pool row
+// `row`; key index of stash slot i is key0 + i.  All NT threads call it.
+template <int NT>
+__device__ __forceinline__ void fused_filter(const uint32_t* stash, int32_t n, int32_t n_valid,
+                                             int32_t key0, uint32_t* scratch, const FusedPool& P,
+                                             int64_t row, int32_t seg) {
+    constexpr int NB = kFilterBins;
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t* hist = scratch;
+    int32_t* wsum = reinterpret_cast<int32_t*>(scratch + NB);
+    uint32_t* misc = scratch + NB + 16;  // kmin, kmax, kept, rank results
+    if (tid == 0) {
+        misc[0] = 0xFFFFFFFFu;
+        misc[1] = 0u;
+        misc[2] = 0u;
+    }
+    for (int i = tid; i < NB; i += NT) hist[i] = 0u;
+    __syncthreads();
+    uint32_t T = 0u;  // keep every valid key
+    if (n_valid > P.r_cap) {
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        for (int i = tid; i < n; i += NT) {
+            const uint32_t k = stash[i];
+            if (k) {
+                lo = min(lo, k);
+                hi = max(hi, k);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+        }
+        if (lane == 0) {
+            atomicMin(&misc[0], lo);
+            atomicMax(&misc[1], hi);
+        }
+        __syncthreads();
+        const uint32_t kmin = misc[0], kmax = misc[1], range = kmax - kmin;
+        if (range == 0u) {
+            T = kmax + 1u;  // more equal keys than fit: drop them all
+        } else {
+            const int hb = 31 - __clz((int)range);
+            const int s1 = max(0, hb - 9);  // (key - kmin) >> s1 < 1024
+            for (int i = tid; i < n; i += NT) {
+                const uint32_t k = stash[i];
+                if (k) atomicAdd(&hist[(k - kmin) >> s1], 1u);
+            }
+            __syncthreads();
+            fz_rank_bin<NT>(hist, P.r_cap + 1, wsum, misc + 3);
+            const uint32_t b1 = misc[3];
+            const int32_t rem = P.r_cap - (int32_t)misc[4];
+            uint64_t t64;
+            if (s1 == 0) {
+                t64 = (uint64_t)kmin + b1 + 1u;  // exact: one key value per bin
+            } else {
+                const int s2 = max(0, s1 - 10);  // sub-bins of bin b1
+                const uint32_t base = b1 << (s1 - s2);
+                for (int i = tid; i < NB; i += NT) hist[i] = 0u;
+                __syncthreads();
+                for (int i = tid; i < n; i += NT) {
+                    const uint32_t k = stash[i];
+                    if (k && ((k - kmin) >> s1) == b1) atomicAdd(&hist[((k - kmin) >> s2) - base], 1u);
+                }
+                __syncthreads();
+                fz_rank_bin<NT>(hist, rem + 1, wsum, misc + 5);
+                t64 = (uint64_t)kmin + ((uint64_t)b1 << s1) + ((uint64_t)(misc[5] + 1u) << s2);
+            }
+            T = (uint32_t)min(t64, (uint64_t)kmax + 1u);
+        }
+    }
+    // emit the kept keys (wave-aggregated slots in the segment's pool run)
+    uint64_t* dst = P.cand + (row * P.n_seg + seg) * (int64_t)P.r_cap;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int32_t b = 0; b < n; b += NT) {
+        const int32_t i = b + tid;
+        const uint32_t k = i < n ? stash[i] : 0u;
+        const bool p = k != 0u && k >= T;
+        const uint64_t m = __ballot(p);
+        if (m == 0) continue;
+        uint32_t at = 0;
+        if (lane == 0) at = atomicAdd(&misc[2], (uint32_t)__popcll(m));
+        const int32_t pos = (int32_t)__builtin_amdgcn_readlane((int)at, 0) + (int32_t)__popcll(m & lt);
+        if (p && pos < P.r_cap) dst[pos] = fz_composite(k, key0 + i);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        P.count[row * P.n_seg + seg] = min((int32_t)misc[2], P.r_cap);
+        P.tau[row * P.n_seg + seg] = T;
     }
 }
 
 // WPR (wave per row): each wave owns one row and walks all its slots;
 // otherwise a workgroup owns one row segment and its 4 waves interleave
 // 32-slot sub-blocks.
-template <int D, int MB, bool FP8, bool BLOCKS, bool WPR>
+template <int D, int MB, bool FP8, bool BLOCKS, bool WPR, bool FUSE = false>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
                                                     int32_t seg_slots) {
+    static_assert(!FUSE || (!BLOCKS && !WPR), "fused mode: contiguous row segments");
     constexpr int KS = D / 16;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m = lane & 31;
     const int hf = lane >> 5;
+    if (FUSE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.fuse_clear = 0;
 
     const int64_t y = WPR ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
     if (y >= n_rows) return;
@@ -146,6 +248,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
     // a global load that the key loads already in flight would hold up
     __shared__ int32_t s_blk[BLOCKS ? kMaxBlkEntries : 1];
     __shared__ int32_t s_last[4];
+    // fused mode: the segment's score keys, then the filter's scratch
+    __shared__ uint32_t s_stash[FUSE ? kFusedSeg : 1];
+    __shared__ uint32_t s_scr[FUSE ? kFilterScratch : 1];
     if constexpr (BLOCKS) {
         const int32_t* blk_row = a.blk + (a.rows.y0 + y) * a.blk_stride;
         const int32_t n_ent = (a.n_cols + bmask) >> a.block_shift;
@@ -210,7 +315,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
         sc += __shfl_xor(sc, 32);
         if (FP8) sc *= scale;
         const int32_t slot = j + m;
-        if (hf == 0 && slot < slot_end) {
+        if constexpr (FUSE) {
+            if (hf == 0 && slot < slot_end) s_stash[slot - slot_begin] = valid ? score_key(sc) : 0u;
+        } else if (hf == 0 && slot < slot_end) {
             if (valid)
                 a.out[y * a.out_stride + slot] = sc;
             else if (a.write_masked)
@@ -259,6 +366,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
             process(f1, j0 + step, v1, s1);
             fetch(f1, j0 + 3 * step, v1, s1);
         }
+    }
+    if constexpr (FUSE) {
+        // every 32-slot sub-block that starts below work_end was stored
+        __syncthreads();
+        const int32_t n_fill = min(slot_end, work_end) - slot_begin;
+        fused_filter<256>(s_stash, n_fill, limit - slot_begin, a.col_key0 + slot_begin, s_scr, a.fuse,
+                          y, blockIdx.y);
     }
 }
 
@@ -324,16 +438,22 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, int MB, bool BLOCKS>
-__global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_rows,
+template <int D, int MB, bool BLOCKS, bool FUSE = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_fp8_kernel(ScoreArgs a, int64_t n_rows,
                                                         int32_t seg_slots) {
+    static_assert(!FUSE || !BLOCKS, "fused mode: contiguous row segments");
     using RG = Fp8Ring<D>;
+    if (FUSE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.fuse_clear = 0;
     constexpr int KS = D / 16;
     __shared__ __align__(16) uint8_t ring[4 * RG::WAVE];
     // the row's q, zero-padded heads; rows padded by 16 bytes so that the
     // fragment reads (32 head rows, one column) spread over the banks
     constexpr int QS = D + 8;
-    __shared__ __align__(16) uint16_t s_q[MB * 32 * QS];
+    // (fused mode: after the q fragments are built, the segment's score
+    // keys take this space)
+    constexpr int QN = FUSE && MB * 32 * QS < 2 * kFusedSeg ? 2 * kFusedSeg : MB * 32 * QS;
+    __shared__ __align__(16) uint16_t s_q[QN];
+    uint32_t* stash = reinterpret_cast<uint32_t*>(s_q);
     __shared__ float s_w[MB * 32];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -471,7 +591,9 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
         bool valid;
         key_of(j + m, valid);
         const int32_t slot = j + m;
-        if (hf == 0 && slot < slot_end) {
+        if constexpr (FUSE) {
+            if (hf == 0 && slot < slot_end) stash[slot - slot_begin] = valid ? score_key(sc) : 0u;
+        } else if (hf == 0 && slot < slot_end) {
             if (valid)
                 a.out[y * a.out_stride + slot] = sc;
             else if (a.write_masked)
@@ -506,6 +628,8 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) wv[mb][j] = s_w[mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3)];
+    // (fused mode: every wave has its fragments before the stash overwrites q)
+    if constexpr (FUSE) __syncthreads();
 
     // two accumulator sets: the MFMAs of sub-block u + 1 are issued before the
     // VALU epilogue of sub-block u, so the matrix and vector pipes overlap
@@ -521,6 +645,14 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(ScoreArgs a, int64_t n_r
     }
     // drain the copies still in flight before the wave's LDS is released
     wait_vmcnt<0>();
+    if constexpr (FUSE) {
+        // every wave's copies have landed: the ring is the filter's scratch
+        static_assert(4 * RG::WAVE >= kFilterScratch * 4, "filter scratch fits the ring");
+        __syncthreads();
+        const int32_t n_fill = min(slot_end, work_end) - slot_begin;
+        fused_filter<256>(stash, n_fill, limit - slot_begin, a.col_key0 + slot_begin,
+                          reinterpret_cast<uint32_t*>(ring), a.fuse, y, blockIdx.y);
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -550,19 +682,6 @@ struct SharedRing {
     static constexpr int NS = 3;              // stages in flight
 };
 constexpr int kSharedRows = 8;  // query rows (waves) per workgroup
-
-// Lanes 0-31 get x + x[lane + 32] (v_permlane32_swap: its second result
-// holds the upper half's values in the lower half).  The builtin exists for
-// the device pass only.
-__device__ __forceinline__ float add_upper_half(float x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                     false);
-    return x + __uint_as_float(sw[1]);
-#else
-    return x;
-#endif
-}
 
 template <int MB, int NW>
 __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int64_t n_rows,
@@ -840,6 +959,22 @@ hipError_t launch_d(const ScoreArgs& a, int64_t n_rows, bool fp8, bool blocks, h
 }
 
 }  // namespace
+
+hipError_t launch_score_fused(const ScoreArgs& a, int64_t n_rows, int32_t n_seg, bool fp8,
+                              hipStream_t stream) {
+    if (n_rows <= 0 || n_seg <= 0) return hipSuccess;
+    if (n_seg > 65535 || a.fuse.cand == nullptr) return hipErrorInvalidValue;
+    // heads padded to 64 (zero q rows and weights add exactly nothing), so
+    // the finish's rescoring uses the same instruction sequence
+    const dim3 grid((unsigned)n_rows, (unsigned)n_seg);
+    if (fp8)
+        hipLaunchKernelGGL((score_fp8_kernel<128, 2, false, true>), grid, dim3(256), 0, stream, a,
+                           n_rows, (int32_t)kFusedSeg);
+    else
+        hipLaunchKernelGGL((score_kernel<128, 2, false, false, false, true>), grid, dim3(256), 0,
+                           stream, a, n_rows, (int32_t)kFusedSeg);
+    return hipGetLastError();
+}
 
 hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
                         hipStream_t stream) {

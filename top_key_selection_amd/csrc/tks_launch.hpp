@@ -9,6 +9,23 @@
 
 namespace tks {
 
+// Fused flat scoring (score.hip): a workgroup scores one segment of
+// kFusedSeg consecutive keys of a row, keeps its best candidates (at most
+// r_cap: every candidate whose score key is at least a threshold T of its
+// own) and writes them, with T, to the row's survivor pool.  Every dropped
+// candidate of the segment has a score key below T (T = 0: none dropped).
+// The finish (fused.hip) selects the row's top-k from the pool; the result
+// is exact when its k-th best survivor's key is at least every segment's T.
+constexpr int kFusedSeg = 4096;
+constexpr int kFusedPoolCap = 4096;  // survivors of one row, all segments together
+struct FusedPool {
+    uint64_t* cand;    // [rows, n_seg, r_cap] composites (score key << 32 | ~index)
+    int32_t* count;    // [rows, n_seg]
+    uint32_t* tau;     // [rows, n_seg]
+    int32_t n_seg;     // segments per row in the pool's layout
+    int32_t r_cap;     // survivors per segment at most
+};
+
 // Scoring of one row chunk against a run of key slots (score.hip).
 //   contiguous mode: slot j is key col_key0 + j of the row's sequence;
 //   block mode:      slot j is key blk[row][j / B] * B + j % B.
@@ -33,6 +50,8 @@ struct ScoreArgs {
     int64_t out_stride;
     int32_t write_masked;
     int32_t stream_keys;    // each key row is read by one query row only (decode)
+    FusedPool fuse;         // fused mode (fuse.cand != null): survivors instead of `out`
+    int32_t* fuse_clear;    // fused mode: a counter the first workgroup sets to 0
 };
 
 // Exact top-k of row candidates (select.hip).  Candidates of a row are the
@@ -115,6 +134,33 @@ struct AttnArgs {
 
 hipError_t launch_score(const ScoreArgs& a, int64_t n_rows, int dim, bool fp8, bool blocks,
                         hipStream_t stream);
+// Fused flat scoring of every row's segments (D = 128; heads padded to 64).
+hipError_t launch_score_fused(const ScoreArgs& a, int64_t n_rows, int32_t n_seg, bool fp8,
+                              hipStream_t stream);
+
+// Finish of the fused flat path (fused.hip): one workgroup per row selects
+// the row's top-k from its survivor pool and checks exactness; a row that
+// fails the check is listed, and a repair kernel redoes it exactly: its
+// keys are rescored tile by tile (kFusedSeg keys, the same MFMA order, so
+// the same scores) into an arena slice and merged by the exact selection
+// with a running list.
+struct FusedFinishArgs {
+    FusedPool pool;
+    SelectArgs sel;        // rows, vis, topk, out_idx / out_val
+    const uint16_t* q;     // (rescoring)
+    const float* w;
+    const void* k;
+    const float* k_scale;
+    int64_t k_seq_len;
+    int32_t heads;
+    float* arena;          // [repair grid, kFusedSeg + 2 * topk] words
+    int32_t* failed;       // [n_rows] rows the finish could not prove
+    int32_t* n_failed;     // cleared by the fused scoring pass
+    int64_t n_rows;
+};
+int32_t fused_finish_grid(int64_t n_rows);
+size_t fused_arena_bytes(int64_t n_rows, int32_t topk);
+hipError_t launch_fused_finish(const FusedFinishArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t n_rows, hipStream_t stream);
 // Selection plan for few long rows (parts = 0: one workgroup per row).
 // parts > 0: a sampled threshold per row, a filter over parts x span column

@@ -49,7 +49,7 @@ class Shape:
 
 
 SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat_workspace",
-           "tks_topk_flat", "tks_topk_scores_workspace", "tks_topk_scores",
+           "tks_topk_flat", "tks_topk_flat_redone", "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
            "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_kv_append",
            "tks_gather_selected", "tks_sparse_attention_workspace", "tks_sparse_attention",
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
     L.tks_topk_flat_workspace.argtypes = [SP, i32, i32, i32]
     L.tks_topk_flat_workspace.restype = sz
     L.tks_topk_flat.argtypes = [SP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
+    L.tks_topk_flat_redone.argtypes = [SP, i32, i32, i32, P, P, P]
     L.tks_topk_scores_workspace.argtypes = [i32, i32, i32]
     L.tks_topk_scores_workspace.restype = sz
     L.tks_topk_scores.argtypes = [P, i32, i32, i64, P, i32, P, P, P, sz, P]
@@ -93,7 +94,8 @@ def lib() -> ctypes.CDLL:
     L.tks_sparse_attention.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, i32, ctypes.c_float, P, P, sz, P]
     L.tks_profile_enable.argtypes = [ctypes.c_int]
     L.tks_profile_read.argtypes = [ctypes.c_char_p, P, P]
-    for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, L.tks_topk_scores, L.tks_hisa_pool_keys, \
+    for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, \
+            L.tks_topk_flat_redone, L.tks_topk_scores, L.tks_hisa_pool_keys, \
             L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append, L.tks_gather_selected, \
             L.tks_sparse_attention:
         s.restype = ctypes.c_int
@@ -130,6 +132,49 @@ def _dev(t, name, dtypes):
     return t
 
 
+def _size(t, name, numel):
+    """Every buffer must hold exactly the elements its layout needs: a short
+    tensor would be read or written past its end by the kernels."""
+    if t is not None and t.numel() != numel:
+        raise ValueError("%s holds %d elements, the layout needs %d" % (name, t.numel(), numel))
+    return t
+
+
+def _ws(ws, need, dev):
+    if ws is None:
+        return workspace(need, dev)
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("workspace holds %d bytes, the call needs %d"
+                         % (ws.numel() * ws.element_size(), need))
+    return ws
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _qwk(shape: Shape, q, w, k, k_scale):
+    """Device, dtype, contiguity and element counts of the indexer inputs."""
+    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
+    _dev(k_scale, "k_scale", (torch.float32,))
+    rows = shape.batch * shape.n_q
+    _size(q, "q", rows * shape.heads * shape.dim)
+    _size(w, "w", rows * shape.heads)
+    _size(k, "k", shape.batch * shape.n_k * shape.dim)
+    if shape.key_dtype == KEY_FP8_E4M3FN and k_scale is None and shape.batch * shape.n_k > 0:
+        raise ValueError("fp8 keys need k_scale")
+    _size(k_scale, "k_scale", shape.batch * shape.n_k)
+
+
+def _out(t, name, numel, dtype, shape3, dev):
+    if t is None:
+        return torch.empty(shape3, dtype=dtype, device=dev)
+    _dev(t, name, (dtype,))
+    return _size(t, name, numel)
+
+
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 _FP8 = (torch.uint8, torch.float8_e4m3fn)
 
@@ -149,10 +194,9 @@ def version() -> int:
 
 def indexer_scores(shape: Shape, q, w, k, k_scale, q_begin, q_count, k_begin, k_count, out=None):
     """fp32 [batch, q_count, k_count] scores, -inf where not visible."""
-    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
-    _dev(k_scale, "k_scale", (torch.float32,))
-    if out is None:
-        out = torch.empty((shape.batch, q_count, k_count), dtype=torch.float32, device=q.device)
+    _qwk(shape, q, w, k, k_scale)
+    out = _out(out, "out", shape.batch * q_count * k_count, torch.float32,
+               (shape.batch, q_count, k_count), q.device)
     S = shape.c()
     _check(lib().tks_indexer_scores(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), q_begin,
                                     q_count, k_begin, k_count, _p(out), _stream()))
@@ -167,20 +211,27 @@ def topk_flat_workspace(shape: Shape, topk, q_chunk=0, k_tile=0) -> int:
 def topk_flat(shape: Shape, q, w, k, k_scale, topk, q_chunk=0, k_tile=0, with_vals=True,
               ws=None, idx=None, vals=None):
     """Flat indexer top-k: (idx int32 [batch, n_q, topk], vals fp32 | None)."""
-    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
-    _dev(k_scale, "k_scale", (torch.float32,))
+    _qwk(shape, q, w, k, k_scale)
     dev = q.device
-    if idx is None:
-        idx = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.int32, device=dev)
-    if vals is None and with_vals:
-        vals = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.float32, device=dev)
-    need = topk_flat_workspace(shape, topk, q_chunk, k_tile)
-    if ws is None:
-        ws = workspace(need, dev)
+    n_out = shape.batch * shape.n_q * topk
+    idx = _out(idx, "idx", n_out, torch.int32, (shape.batch, shape.n_q, topk), dev)
+    if vals is not None or with_vals:
+        vals = _out(vals, "vals", n_out, torch.float32, (shape.batch, shape.n_q, topk), dev)
+    ws = _ws(ws, topk_flat_workspace(shape, topk, q_chunk, k_tile), dev)
     S = shape.c()
     _check(lib().tks_topk_flat(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), topk, q_chunk,
-                               k_tile, _p(idx), _p(vals), _p(ws), ws.numel(), _stream()))
+                               k_tile, _p(idx), _p(vals), _p(ws), _nbytes(ws), _stream()))
     return idx, vals
+
+
+def topk_flat_redone(shape: Shape, topk, ws, q_chunk=0, k_tile=0) -> int:
+    """Rows of the last topk_flat call on workspace `ws` that the fused form
+    redid by exact rescoring (0 for the tiled form).  Synchronises."""
+    n = ctypes.c_int32()
+    S = shape.c()
+    _check(lib().tks_topk_flat_redone(ctypes.byref(S), topk, q_chunk, k_tile, _p(ws),
+                                      ctypes.byref(n), _stream()))
+    return n.value
 
 
 def topk_scores_workspace(n_rows, n_cols, topk) -> int:
@@ -203,19 +254,25 @@ def topk_scores(scores, topk, row_len=None, with_vals=True, ws=None, idx=None, v
     for t, name in ((idx, "idx"), (vals, "vals")):
         if t is not None and t.numel() != n_rows * topk:
             raise ValueError("%s must hold n_rows x topk = %d elements" % (name, n_rows * topk))
-    if ws is None:
-        ws = workspace(topk_scores_workspace(n_rows, n_cols, topk), dev)
+    _size(row_len, "row_len", n_rows)
+    ws = _ws(ws, topk_scores_workspace(n_rows, n_cols, topk), dev)
     _check(lib().tks_topk_scores(_p(scores), n_rows, n_cols, scores.stride(0), _p(row_len), topk,
-                                 _p(idx), _p(vals), _p(ws), ws.numel(), _stream()))
+                                 _p(idx), _p(vals), _p(ws), _nbytes(ws), _stream()))
     return idx, vals
 
 
 def hisa_pool_keys(shape: Shape, k, k_scale, block, pooled=None):
     """bf16 [batch, n_k // block, dim] pooled keys."""
     _dev(k, "k", _key_dtypes(shape)), _dev(k_scale, "k_scale", (torch.float32,))
+    _size(k, "k", shape.batch * shape.n_k * shape.dim)
+    _size(k_scale, "k_scale", shape.batch * shape.n_k)
+    if block <= 0:
+        raise ValueError("block must be positive")
+    nb = shape.n_k // block
     if pooled is None:
-        pooled = torch.empty((shape.batch, shape.n_k // block, shape.dim), dtype=torch.bfloat16,
-                             device=k.device)
+        pooled = torch.empty((shape.batch, nb, shape.dim), dtype=torch.bfloat16, device=k.device)
+    _dev(pooled, "pooled", _BF16)
+    _size(pooled, "pooled", shape.batch * nb * shape.dim)
     S = shape.c()
     _check(lib().tks_hisa_pool_keys(ctypes.byref(S), _p(k), _p(k_scale), block, _p(pooled),
                                     _stream()))
@@ -232,6 +289,13 @@ def kv_append(shape: Shape, raw, raw_len, k, k_scale=None, raw_tail=None, block=
     _dev(pooled, "pooled", _BF16)
     if raw.dim() != 3 or raw.shape[0] != shape.batch or raw.shape[2] != shape.dim:
         raise ValueError("raw must be [batch, n_new, dim]")
+    _size(k, "k", shape.batch * shape.n_k * shape.dim)
+    if shape.key_dtype == KEY_FP8_E4M3FN:
+        _size(k_scale, "k_scale", shape.batch * shape.n_k)
+    if shape.causal_ratio > 1:
+        _size(raw_tail, "raw_tail", shape.batch * shape.causal_ratio * shape.dim)
+    if block > 0:
+        _size(pooled, "pooled", shape.batch * (shape.n_k // block) * shape.dim)
     S = shape.c()
     _check(lib().tks_kv_append(ctypes.byref(S), _p(raw), raw.shape[1], int(raw_len), _p(raw_tail),
                                _p(k), _p(k_scale), int(block), _p(pooled), _stream()))
@@ -250,6 +314,8 @@ def gather_selected(kv, idx, out=None):
     if out is None:
         out = torch.empty((batch, idx.shape[1], idx.shape[2]) + tuple(kv.shape[2:]), dtype=kv.dtype,
                           device=kv.device)
+    if not out.is_cuda or not out.is_contiguous() or _nbytes(out) != idx.numel() * row_bytes:
+        raise ValueError("out must be a contiguous device tensor of batch x n_q x topk rows")
     _check(lib().tks_gather_selected(_p(kv), batch, n_kv, row_bytes, _p(idx), idx.shape[1], idx.shape[2],
                                      _p(out), _stream()))
     return out
@@ -264,14 +330,17 @@ def sparse_attention(q, k, v, idx, scale, out=None, ws=None):
     q bf16 [batch, n_q, heads, 128]; k, v bf16 [batch, n_kv, 128]; idx int32
     [batch, n_q, topk]."""
     _dev(q, "q", _BF16), _dev(k, "k", _BF16), _dev(v, "v", _BF16), _dev(idx, "idx", (torch.int32,))
+    if q.dim() != 4 or k.dim() != 3 or tuple(v.shape) != tuple(k.shape) or idx.dim() != 3:
+        raise ValueError("q [batch, n_q, heads, dim], k / v [batch, n_kv, dim], idx [batch, n_q, topk]")
     batch, n_q, heads, dim = q.shape
+    if k.shape[0] != batch or k.shape[2] != dim or tuple(idx.shape[:2]) != (batch, n_q):
+        raise ValueError("q, k / v and idx disagree on batch, n_q or dim")
     topk = idx.shape[2]
-    if out is None:
-        out = torch.empty((batch, n_q, heads, dim), dtype=torch.float32, device=q.device)
-    if ws is None:
-        ws = workspace(sparse_attention_workspace(batch, n_q, heads, topk), q.device)
+    out = _out(out, "out", batch * n_q * heads * dim, torch.float32, (batch, n_q, heads, dim),
+               q.device)
+    ws = _ws(ws, sparse_attention_workspace(batch, n_q, heads, topk), q.device)
     _check(lib().tks_sparse_attention(_p(q), _p(k), _p(v), batch, n_q, heads, dim, k.shape[1], _p(idx), topk,
-                                      float(scale), _p(out), _p(ws), ws.numel(), _stream()))
+                                      float(scale), _p(out), _p(ws), _nbytes(ws), _stream()))
     return out
 
 
@@ -288,18 +357,23 @@ def hisa_block_select(shape: Shape, q, w, pooled, block, m_scored, force_flags, 
                       ws=None, blk=None, blk_vals=None):
     """(blk int32 [batch, n_q, m_total] ascending, blk_vals fp32 | None)."""
     _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(pooled, "pooled", _BF16)
+    rows = shape.batch * shape.n_q
+    _size(q, "q", rows * shape.heads * shape.dim)
+    _size(w, "w", rows * shape.heads)
+    if block <= 0:
+        raise ValueError("block must be positive")
+    _size(pooled, "pooled", shape.batch * (shape.n_k // block) * shape.dim)
     m_total = m_total_of(m_scored, force_flags)
     dev = q.device
-    if blk is None:
-        blk = torch.empty((shape.batch, shape.n_q, m_total), dtype=torch.int32, device=dev)
-    if blk_vals is None and with_vals:
-        blk_vals = torch.empty((shape.batch, shape.n_q, m_total), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = workspace(hisa_block_select_workspace(shape, block, m_scored), dev)
+    blk = _out(blk, "blk", rows * m_total, torch.int32, (shape.batch, shape.n_q, m_total), dev)
+    if blk_vals is not None or with_vals:
+        blk_vals = _out(blk_vals, "blk_vals", rows * m_total, torch.float32,
+                        (shape.batch, shape.n_q, m_total), dev)
+    ws = _ws(ws, hisa_block_select_workspace(shape, block, m_scored), dev)
     S = shape.c()
     _check(lib().tks_hisa_block_select(ctypes.byref(S), _p(q), _p(w), _p(pooled), block, m_scored,
                                        force_flags, _p(blk), _p(blk_vals), m_total, _p(ws),
-                                       ws.numel(), _stream()))
+                                       _nbytes(ws), _stream()))
     return blk, blk_vals
 
 
@@ -311,20 +385,20 @@ def hisa_refine_workspace(shape: Shape, block, m_total, topk, q_chunk=0) -> int:
 def hisa_refine_topk(shape: Shape, q, w, k, k_scale, block, blk, topk, q_chunk=0, with_vals=True,
                      ws=None, idx=None, vals=None):
     """(idx int32 [batch, n_q, topk], vals fp32 | None) inside the kept blocks."""
-    _dev(q, "q", _BF16), _dev(w, "w", (torch.float32,)), _dev(k, "k", _key_dtypes(shape))
-    _dev(k_scale, "k_scale", (torch.float32,)), _dev(blk, "blk", (torch.int32,))
-    m_total = blk.shape[-1]
+    _qwk(shape, q, w, k, k_scale)
+    _dev(blk, "blk", (torch.int32,))
+    rows = shape.batch * shape.n_q
+    m_total = blk.shape[-1] if blk.dim() > 0 else 0
+    _size(blk, "blk", rows * m_total)
     dev = q.device
-    if idx is None:
-        idx = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.int32, device=dev)
-    if vals is None and with_vals:
-        vals = torch.empty((shape.batch, shape.n_q, topk), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = workspace(hisa_refine_workspace(shape, block, m_total, topk, q_chunk), dev)
+    idx = _out(idx, "idx", rows * topk, torch.int32, (shape.batch, shape.n_q, topk), dev)
+    if vals is not None or with_vals:
+        vals = _out(vals, "vals", rows * topk, torch.float32, (shape.batch, shape.n_q, topk), dev)
+    ws = _ws(ws, hisa_refine_workspace(shape, block, m_total, topk, q_chunk), dev)
     S = shape.c()
     _check(lib().tks_hisa_refine_topk(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), block,
                                       _p(blk), m_total, topk, q_chunk, _p(idx), _p(vals), _p(ws),
-                                      ws.numel(), _stream()))
+                                      _nbytes(ws), _stream()))
     return idx, vals
 
 
