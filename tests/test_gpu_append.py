@@ -110,7 +110,7 @@ def test_split_appends_equal_oracle_compression_and_pooling(batch, dim, m, fp8, 
     c.check(raw, what="end")
 
 
-@pytest.mark.parametrize("m,fp8", [(1, True), (4, False), (4, True)])
+@pytest.mark.parametrize("m,fp8", [(1, True), (1, False), (4, False), (4, True)])
 def test_single_token_appends_cross_block_boundaries(m, fp8):
     batch, dim, block = 2, 128, 32
     n_raw = m * (2 * block + 5)

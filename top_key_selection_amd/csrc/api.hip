@@ -273,10 +273,15 @@ size_t tks_topk_flat_workspace(const tks_shape* s, int32_t topk, int32_t q_chunk
     return plan_flat(s, topk, q_chunk, k_tile).bytes;
 }
 
-int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void* k,
-                  const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
-                  int32_t* idx, float* vals, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the flat top-k (shared by both entry points); sets
+// *rows and *plan.  rows == 0 means nothing to do.
+int flat_checks(const tks_shape* s, const void* q, const float* w, const void* k,
+                const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                const int32_t* idx, const float* vals, int64_t* rows, FlatPlan* plan) {
     int rc = check_shape(s, true);
     if (rc) return rc;
     if (topk < 1 || topk > kMaxTopk)
@@ -284,18 +289,47 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
     if (q_chunk < 0 || k_tile < 0) return fail(TKS_EINVAL, "negative q_chunk or k_tile");
     if (k_tile > 0 && k_tile % 32 != 0)
         return fail(TKS_EINVAL, "k_tile = %d (must be a multiple of 32)", k_tile);
-    const int64_t rows = (int64_t)s->batch * s->n_q;
-    if (rows == 0) return TKS_OK;
+    *rows = (int64_t)s->batch * s->n_q;
+    if (*rows == 0) return TKS_OK;
     if ((rc = check_qwk(s, q, w, k, k_scale))) return rc;
     if (!idx || !aligned(idx, 4) || (vals && !aligned(vals, 4)))
         return fail(TKS_EINVAL, "idx is NULL, or idx / vals misaligned");
-    const FlatPlan p = plan_flat(s, topk, q_chunk, k_tile);
+    *plan = plan_flat(s, topk, q_chunk, k_tile);
+    return TKS_OK;
+}
+
+int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void* k,
+                  const float* k_scale, int32_t topk, int32_t* idx, float* vals, const FlatPlan& p,
+                  char* ws, hipStream_t stream);
+
+}  // namespace
+
+extern "C" {
+
+int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void* k,
+                  const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                  int32_t* idx, float* vals, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    int64_t rows = 0;
+    FlatPlan p{};
+    int rc = flat_checks(s, q, w, k, k_scale, topk, q_chunk, k_tile, idx, vals, &rows, &p);
+    if (rc || rows == 0) return rc;
     if (!workspace || workspace_bytes < p.bytes)
         return fail(TKS_EWORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                     p.bytes);
     if (!aligned(workspace, 256)) return fail(TKS_EINVAL, "workspace must be 256-byte aligned");
+    return topk_flat_run(s, q, w, k, k_scale, topk, idx, vals, p, static_cast<char*>(workspace),
+                         stream);
+}
 
-    char* ws = static_cast<char*>(workspace);
+}  // extern "C"
+
+namespace {
+
+int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void* k,
+                  const float* k_scale, int32_t topk, int32_t* idx, float* vals, const FlatPlan& p,
+                  char* ws, hipStream_t stream) {
+    const int64_t rows = p.rows;
     if (p.fused) {
         const bool fp8k = s->key_dtype == TKS_KEY_FP8_E4M3FN;
         const tks::FusedPool pool{reinterpret_cast<uint64_t*>(ws + p.off_cand),
@@ -412,6 +446,10 @@ int tks_topk_flat(const tks_shape* s, const void* q, const float* w, const void*
     }
     return TKS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int tks_topk_flat_redone(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile,
                          const void* workspace, int32_t* n_redone, hipStream_t stream) {

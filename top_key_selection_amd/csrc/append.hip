@@ -23,6 +23,11 @@
 // call also moves the staging buffer: its threads read the old staged keys
 // of that group before they stage the new ones, and no other thread touches
 // a slot.
+//
+// A call that stays inside one block per sequence (a decode append) takes a
+// workgroup per sequence instead: all its threads copy the block's earlier
+// compressed keys to LDS at once (one memory round trip instead of one per
+// few keys), then the D/8 owner threads sum them from LDS in key order.
 #include "tks_launch.hpp"
 
 namespace tks {
@@ -31,6 +36,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kAhead = 4;  // raw (or cached) key rows in flight per thread
+constexpr int kStageMax = 255;  // earlier keys of a block staged in LDS (block <= 256)
 
 // fp64 -> bf16, nearest-even: round-to-odd to fp32 (24 bits >= 8 + 2), then
 // nearest-even to bf16, which keeps the rounding single.
@@ -79,12 +85,13 @@ __device__ inline void add_fp8x8(double* acc, uint32_t c0, uint32_t c1, float sc
     }
 }
 
-template <bool FP8, int D, bool M1>
+template <bool FP8, int D, bool M1, bool STAGE>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     constexpr int TPG = D / 8;  // threads per key (8 dims each)
     const int64_t gt = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t job = gt / TPG;
-    const int piece = (int)(gt % TPG);
+    // STAGE: one job per workgroup; threads past TPG only help stage
+    const int64_t job = STAGE ? (int64_t)blockIdx.x : gt / TPG;
+    const int piece = STAGE ? (int)threadIdx.x : (int)(gt % TPG);
     if (job >= (int64_t)a.batch * a.n_jobs) return;
     const int32_t b = (int32_t)(job / a.n_jobs);
     const int32_t J = a.J0 + (int32_t)(job % a.n_jobs);
@@ -100,7 +107,47 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     for (int e = 0; e < 8; ++e) pacc[e] = 0.0;
 
     // compressed keys of block J that earlier calls wrote, in key order
-    if (pool) {
+    if (STAGE && pool) {
+        constexpr int KB = FP8 ? D : 2 * D;  // bytes per cached key
+        __shared__ __align__(16) uint8_t s_k[STAGE ? kStageMax * KB : 16];
+        __shared__ float s_s[STAGE ? kStageMax : 1];
+        const int32_t n_back = gs - J * a.span;  // < block size <= 256
+        const uint8_t* src = static_cast<const uint8_t*>(a.k) + (kbase + J * a.span) * KB;
+        for (int o = threadIdx.x * 16; o < n_back * KB; o += kThreads * 16)
+            *reinterpret_cast<u32x4*>(s_k + o) = *reinterpret_cast<const u32x4*>(src + o);
+        if (FP8)
+            for (int i = threadIdx.x; i < n_back; i += kThreads) s_s[i] = a.k_scale[kbase + J * a.span + i];
+        __syncthreads();
+        if (piece >= TPG) return;
+        // eight rows' LDS reads issued before their sums (the sums stay in
+        // key order)
+        constexpr int U = 8;
+        for (int32_t i0 = 0; i0 < n_back; i0 += U) {
+            if constexpr (FP8) {
+                u32x2 c[U];
+                float sc[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int32_t i = min(i0 + u, n_back - 1);
+                    c[u] = *reinterpret_cast<const u32x2*>(s_k + i * KB + 8 * piece);
+                    sc[u] = s_s[i];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (i0 + u < n_back) add_fp8x8(pacc, c[u][0], c[u][1], sc[u]);
+            } else {
+                u32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[u] = *reinterpret_cast<const u32x4*>(s_k + min(i0 + u, n_back - 1) * KB + 16 * piece);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (i0 + u < n_back) add_bf16x8(pacc, v[u]);
+            }
+        }
+    } else if (STAGE && piece >= TPG) {
+        return;
+    } else if (pool) {
         for (int32_t g = J * a.span; g < gs; g += kAhead) {
             if constexpr (FP8) {
                 u32x2 c[kAhead];
@@ -271,12 +318,21 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
 template <bool FP8, int D>
 void launch_d(const AppendArgs& a, hipStream_t stream) {
     constexpr int TPG = D / 8;
+    if (a.n_jobs == 1 && a.pooled != nullptr && a.span <= kStageMax + 1) {
+        // one block per sequence (decode): a workgroup per sequence
+        const dim3 grid((unsigned)a.batch);
+        if (a.m == 1)
+            hipLaunchKernelGGL((append_kernel<FP8, D, true, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((append_kernel<FP8, D, false, true>), grid, dim3(kThreads), 0, stream, a);
+        return;
+    }
     const int64_t threads = (int64_t)a.batch * a.n_jobs * TPG;
     const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
     if (a.m == 1)
-        hipLaunchKernelGGL((append_kernel<FP8, D, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((append_kernel<FP8, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((append_kernel<FP8, D, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((append_kernel<FP8, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
 template <bool FP8>

@@ -108,6 +108,28 @@ __device__ void redo_row(const FusedFinishArgs& a, SelectLds& L, float* arena, i
     float* tile = arena;
     float* run_val = arena + kFusedSeg;
     int32_t* run_idx = reinterpret_cast<int32_t*>(arena + kFusedSeg + K);
+    // the tiled exact selection of one row (chunk of one row at global row
+    // y), the running list in the arena
+    auto tile_args = [&](int32_t tb, int32_t te) {
+        SelectArgs t = a.sel;
+        t.scores = tile;
+        t.score_stride = kFusedSeg;
+        t.n_cols = te - tb;
+        t.rows = RowMap{a.sel.rows.y0 + y, a.sel.rows.rows_per_seq, a.sel.rows.t_begin, a.sel.rows.n_q};
+        t.col_key0 = tb;
+        t.col_lo = 0;
+        t.row_len = nullptr;
+        t.blocks_mode = 0;
+        t.prior_val = run_val;
+        t.prior_idx = run_idx;
+        t.run_val = run_val;
+        t.run_idx = run_idx;
+        t.tile_begin = tb;
+        t.tile_end = te >= n_vis ? INT32_MAX : te;
+        t.always_final = 0;
+        t.blockselect = 0;
+        return t;
+    };
     for (int32_t tb = 0; tb < n_vis; tb += kFusedSeg) {
         const int32_t te = min(n_vis, tb + kFusedSeg);
         // (the selection of the previous tile is done with L)
@@ -116,23 +138,7 @@ __device__ void redo_row(const FusedFinishArgs& a, SelectLds& L, float* arena, i
         rescore_tile<FP8, NT>(a, R, kseq, tb, te - tb, tile);
         __threadfence();
         __syncthreads();
-        SelectArgs s = a.sel;
-        s.scores = tile;
-        s.score_stride = kFusedSeg;
-        s.n_cols = te - tb;
-        s.rows = RowMap{a.sel.rows.y0 + y, a.sel.rows.rows_per_seq, a.sel.rows.t_begin, a.sel.rows.n_q};
-        s.col_key0 = tb;
-        s.col_lo = 0;
-        s.row_len = nullptr;
-        s.blocks_mode = 0;
-        s.prior_val = run_val;
-        s.prior_idx = run_idx;
-        s.run_val = run_val;
-        s.run_idx = run_idx;
-        s.tile_begin = tb;
-        s.tile_end = te >= n_vis ? INT32_MAX : te;
-        s.always_final = 0;
-        s.blockselect = 0;
+        const SelectArgs s = tile_args(tb, te);
         RowCtx r;
         int32_t count;
         setup_row<NT>(s, r, L, 0, count);
@@ -199,11 +205,24 @@ __global__ __launch_bounds__(NT) void fused_finish_kernel(FusedFinishArgs a) {
         const uint32_t tau_max = s_tau;
         bool ok = total <= kCap;
         if (ok) {
-            // the pool, compacted into the candidate list
+            // the pool, compacted into the candidate list (a wave per
+            // segment, four loads per lane issued before any is stored)
             for (int g = wave; g < n_seg; g += NW) {
                 const uint64_t* src = P.cand + (y * P.n_seg + g) * (int64_t)P.r_cap;
                 const int32_t o = s_off[g], c = s_cnt[g];
-                for (int i = lane; i < c; i += 64) L.u[kMaxK + o + i] = src[i];
+                for (int b = 0; b < c; b += 256) {
+                    uint64_t v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = b + j * 64 + lane;
+                        v[j] = i < c ? src[i] : 0ull;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = b + j * 64 + lane;
+                        if (i < c) L.u[kMaxK + o + i] = v[j];
+                    }
+                }
             }
         }
         __syncthreads();
@@ -245,7 +264,8 @@ __global__ __launch_bounds__(NT) void fused_finish_kernel(FusedFinishArgs a) {
 // (rescoring + tiled exact selection).  The failed-row counter is cleared
 // by the fused scoring pass that precedes the finish.
 template <bool FP8, int NT>
-__global__ __launch_bounds__(NT) void fused_repair_kernel(FusedFinishArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_repair_kernel(
+    FusedFinishArgs a) {
     __shared__ SelectLds L;
     const int32_t n = *a.n_failed;
     float* arena = a.arena + (int64_t)blockIdx.x * arena_stride(a.sel.topk);
@@ -256,7 +276,9 @@ __global__ __launch_bounds__(NT) void fused_repair_kernel(FusedFinishArgs a) {
     }
 }
 
-constexpr int32_t kFinishGridMax = 512;
+// Repair workgroups: a small persistent grid (rows that fail the proof are
+// rare; a launch that finds none should cost little).
+constexpr int32_t kFinishGridMax = 16;
 
 }  // namespace
 

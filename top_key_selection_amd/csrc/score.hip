@@ -32,150 +32,131 @@ constexpr int kMaxBlkEntries = 512;
 
 // ------------------------------------------------------------------------
 // Fused segment filter.  A workgroup that scored one segment of a row holds
-// the segment's score keys in LDS (key 0: no candidate).  It keeps at most
-// r_cap of them without sorting: the keep threshold T is the smallest key
-// value that at most r_cap keys reach, found by two rounds of a 1024-bin
-// histogram over the key range [kmin, kmax] (the second round inside the
-// first round's boundary bin; when that bin is wider than one key value the
-// whole boundary sub-bin is dropped, which keeps fewer, never more).  Keys
-// at or above T leave as composites (score key << 32 | ~index), and T goes
-// with them: every dropped key of the segment is below T.
+// the segment's score keys in LDS (key 0: no candidate) and the range of
+// its valid keys (tracked while scoring).  It keeps at most r_cap of them
+// without sorting: the segment's score range [vmin, vmax] is cut into 256
+// equal bins (a non-decreasing function of the score), and the kept keys
+// are those of the top bins that together hold at most r_cap.  Every
+// dropped key lies in a lower bin, so it is below every kept key: the
+// segment's threshold T (the smallest kept key, or above vmax when none is
+// kept) bounds every dropped key from above, which is all the finish needs
+// to prove its result exact.  A segment that fits keeps everything (T = 0).
 
-constexpr int kFilterBins = 1024;
-constexpr int kFilterScratch = kFilterBins + 32;  // words: bins, wave sums, results
+constexpr int kFilterScratch = 256 + 32;  // words of a 256-thread filter: bins, wave sums, results
 
 __device__ __forceinline__ uint64_t fz_composite(uint32_t key, int32_t idx) {
     return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-// Bin of hist[0, NB) holding the R-th largest entry (1-based; the total is
-// at least R): res[0] = bin, res[1] = entries in the bins above it.
-template <int NT>
-__device__ __forceinline__ void fz_rank_bin(const uint32_t* hist, int32_t R, int32_t* wsum,
-                                            uint32_t* res) {
-    constexpr int NB = kFilterBins, PER = NB / NT, NW = NT / 64;
-    static_assert(PER * NT == NB, "bins per thread");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int32_t c[PER];
-    int32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = (int32_t)hist[NB - 1 - (PER * tid + i)];  // descending bins
-        sum += c[i];
-    }
-    int32_t inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int32_t v = __shfl_up(inc, o);
-        if (lane >= o) inc += v;
-    }
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) inc += w < wave ? wsum[w] : 0;
-    int32_t cum = inc - sum;
-    if (cum < R && R <= inc) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (cum < R && R <= cum + c[i]) {
-                res[0] = (uint32_t)(NB - 1 - (PER * tid + i));
-                res[1] = (uint32_t)cum;
-            }
-            cum += c[i];
-        }
-    }
-    __syncthreads();
+// key_score of tks_device.hpp, for the bin of a key
+__device__ __forceinline__ float fz_value(uint32_t key) {
+    const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+    return __uint_as_float(u);
 }
 
-// Filter stash[0, n) (n_valid valid keys) of segment `seg` of pool row
-// `row`; key index of stash slot i is key0 + i.  All NT threads call it.
+// Filter stash[0, n) (n_valid valid keys, whose smallest and largest keys
+// this thread saw are lo / hi) of segment `seg` of pool row `row`; the key
+// index of stash slot i is key0 + i.  NT threads call it (NT bins, one per
+// thread in the scan); n <= kFusedSeg; scratch holds NT + 32 words.
 template <int NT>
 __device__ __forceinline__ void fused_filter(const uint32_t* stash, int32_t n, int32_t n_valid,
                                              int32_t key0, uint32_t* scratch, const FusedPool& P,
-                                             int64_t row, int32_t seg) {
-    constexpr int NB = kFilterBins;
-    const int tid = threadIdx.x, lane = tid & 63;
+                                             int64_t row, int32_t seg, uint32_t lo, uint32_t hi) {
+    constexpr int NB = NT, PER = kFusedSeg / NT;
+    static_assert(PER % 4 == 0, "16-byte stash reads");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t* hist = scratch;
     int32_t* wsum = reinterpret_cast<int32_t*>(scratch + NB);
-    uint32_t* misc = scratch + NB + 16;  // kmin, kmax, kept, rank results
+    uint32_t* misc = scratch + NB + 16;  // kmin, kmax, kept, kept min, keep-from bin
+    // this thread's keys: slots c * 4 NT + 4 * tid + j (16-byte LDS reads)
+    uint32_t key[PER];
+#pragma unroll
+    for (int c = 0; c < PER / 4; ++c) {
+        const int i0 = c * (4 * NT) + 4 * tid;
+        const u32x4 v = i0 < n ? *reinterpret_cast<const u32x4*>(stash + i0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) key[4 * c + j] = i0 + j < n ? v[j] : 0u;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    }
     if (tid == 0) {
         misc[0] = 0xFFFFFFFFu;
         misc[1] = 0u;
         misc[2] = 0u;
+        misc[3] = 0xFFFFFFFFu;
+        misc[4] = 0u;  // keep from bin 0: every valid key
     }
-    for (int i = tid; i < NB; i += NT) hist[i] = 0u;
+    hist[tid] = 0u;
     __syncthreads();
-    uint32_t T = 0u;  // keep every valid key
-    if (n_valid > P.r_cap) {
-        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-        for (int i = tid; i < n; i += NT) {
-            const uint32_t k = stash[i];
-            if (k) {
-                lo = min(lo, k);
-                hi = max(hi, k);
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-        }
-        if (lane == 0) {
-            atomicMin(&misc[0], lo);
-            atomicMax(&misc[1], hi);
-        }
-        __syncthreads();
-        const uint32_t kmin = misc[0], kmax = misc[1], range = kmax - kmin;
-        if (range == 0u) {
-            T = kmax + 1u;  // more equal keys than fit: drop them all
-        } else {
-            const int hb = 31 - __clz((int)range);
-            const int s1 = max(0, hb - 9);  // (key - kmin) >> s1 < 1024
-            for (int i = tid; i < n; i += NT) {
-                const uint32_t k = stash[i];
-                if (k) atomicAdd(&hist[(k - kmin) >> s1], 1u);
-            }
-            __syncthreads();
-            fz_rank_bin<NT>(hist, P.r_cap + 1, wsum, misc + 3);
-            const uint32_t b1 = misc[3];
-            const int32_t rem = P.r_cap - (int32_t)misc[4];
-            uint64_t t64;
-            if (s1 == 0) {
-                t64 = (uint64_t)kmin + b1 + 1u;  // exact: one key value per bin
-            } else {
-                const int s2 = max(0, s1 - 10);  // sub-bins of bin b1
-                const uint32_t base = b1 << (s1 - s2);
-                for (int i = tid; i < NB; i += NT) hist[i] = 0u;
-                __syncthreads();
-                for (int i = tid; i < n; i += NT) {
-                    const uint32_t k = stash[i];
-                    if (k && ((k - kmin) >> s1) == b1) atomicAdd(&hist[((k - kmin) >> s2) - base], 1u);
-                }
-                __syncthreads();
-                fz_rank_bin<NT>(hist, rem + 1, wsum, misc + 5);
-                t64 = (uint64_t)kmin + ((uint64_t)b1 << s1) + ((uint64_t)(misc[5] + 1u) << s2);
-            }
-            T = (uint32_t)min(t64, (uint64_t)kmax + 1u);
-        }
+    if (lane == 0) {
+        atomicMin(&misc[0], lo);
+        atomicMax(&misc[1], hi);
     }
+    __syncthreads();
+    const uint32_t kmin = misc[0], kmax = misc[1];
+    const float vmin = fz_value(kmin);
+    const float range = fz_value(kmax) - vmin;
+    // (a range that overflows, or so narrow that the bin scale overflows,
+    // keeps no key; the finish then rescores the row)
+    float scale = range > 0.0f && range < __builtin_inff() ? (float)NB / range : 0.0f;
+    if (!(scale < __builtin_inff())) scale = 0.0f;
+    const bool filter = n_valid > P.r_cap;
+    auto bin_of = [&](uint32_t k) {
+        return (int32_t)fminf((fz_value(k) - vmin) * scale, (float)(NB - 1));
+    };
+    if (filter && scale > 0.0f) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (key[e]) atomicAdd(&hist[bin_of(key[e])], 1u);
+        __syncthreads();
+        // bins from the top: the first bin at which the count passes r_cap
+        // is the boundary; keep the bins above it
+        const int32_t c = (int32_t)hist[NB - 1 - tid];
+        int32_t inc = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t v = __shfl_up(inc, o);
+            if (lane >= o) inc += v;
+        }
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) inc += w < wave ? wsum[w] : 0;
+        if (inc - c <= P.r_cap && inc > P.r_cap) misc[4] = (uint32_t)(NB - tid);
+    } else if (filter) {
+        if (tid == 0) misc[4] = NB;  // keep none
+    }
+    __syncthreads();
+    const int32_t keep_from = (int32_t)misc[4];
     // emit the kept keys (wave-aggregated slots in the segment's pool run)
     uint64_t* dst = P.cand + (row * P.n_seg + seg) * (int64_t)P.r_cap;
     const uint64_t lt = (1ull << lane) - 1ull;
-    for (int32_t b = 0; b < n; b += NT) {
-        const int32_t i = b + tid;
-        const uint32_t k = i < n ? stash[i] : 0u;
-        const bool p = k != 0u && k >= T;
+    uint32_t kept_min = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const uint32_t k = key[e];
+        const bool p = k != 0u && (!filter || (keep_from < NB && scale > 0.0f && bin_of(k) >= keep_from));
         const uint64_t m = __ballot(p);
         if (m == 0) continue;
+        if (p) kept_min = min(kept_min, k);
         uint32_t at = 0;
         if (lane == 0) at = atomicAdd(&misc[2], (uint32_t)__popcll(m));
         const int32_t pos = (int32_t)__builtin_amdgcn_readlane((int)at, 0) + (int32_t)__popcll(m & lt);
+        const int i = (e >> 2) * (4 * NT) + 4 * tid + (e & 3);
         if (p && pos < P.r_cap) dst[pos] = fz_composite(k, key0 + i);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) kept_min = min(kept_min, (uint32_t)__shfl_xor((int)kept_min, o));
+    if (lane == 0) atomicMin(&misc[3], kept_min);
     __syncthreads();
     if (tid == 0) {
-        P.count[row * P.n_seg + seg] = min((int32_t)misc[2], P.r_cap);
-        P.tau[row * P.n_seg + seg] = T;
+        const uint32_t kept = misc[2];
+        P.count[row * P.n_seg + seg] = min((int32_t)kept, P.r_cap);
+        // every dropped key is below the smallest kept one (or above none)
+        P.tau[row * P.n_seg + seg] = !filter ? 0u : kept > 0 ? misc[3] : kmax + 1u;
     }
 }
 
@@ -248,9 +229,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
     // a global load that the key loads already in flight would hold up
     __shared__ int32_t s_blk[BLOCKS ? kMaxBlkEntries : 1];
     __shared__ int32_t s_last[4];
-    // fused mode: the segment's score keys, then the filter's scratch
-    __shared__ uint32_t s_stash[FUSE ? kFusedSeg : 1];
+    // fused mode: the segment's score keys, then the filter's scratch; the
+    // smallest / largest valid key this lane stored
+    __shared__ __align__(16) uint32_t s_stash[FUSE ? kFusedSeg : 4];
     __shared__ uint32_t s_scr[FUSE ? kFilterScratch : 1];
+    uint32_t f_lo = 0xFFFFFFFFu, f_hi = 0u;
     if constexpr (BLOCKS) {
         const int32_t* blk_row = a.blk + (a.rows.y0 + y) * a.blk_stride;
         const int32_t n_ent = (a.n_cols + bmask) >> a.block_shift;
@@ -316,7 +299,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
         if (FP8) sc *= scale;
         const int32_t slot = j + m;
         if constexpr (FUSE) {
-            if (hf == 0 && slot < slot_end) s_stash[slot - slot_begin] = valid ? score_key(sc) : 0u;
+            const uint32_t key = valid ? score_key(sc) : 0u;
+            if (hf == 0 && slot < slot_end) s_stash[slot - slot_begin] = key;
+            if (valid) {
+                f_lo = min(f_lo, key);
+                f_hi = max(f_hi, key);
+            }
         } else if (hf == 0 && slot < slot_end) {
             if (valid)
                 a.out[y * a.out_stride + slot] = sc;
@@ -372,7 +360,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
         __syncthreads();
         const int32_t n_fill = min(slot_end, work_end) - slot_begin;
         fused_filter<256>(s_stash, n_fill, limit - slot_begin, a.col_key0 + slot_begin, s_scr, a.fuse,
-                          y, blockIdx.y);
+                          y, blockIdx.y, f_lo, f_hi);
     }
 }
 
@@ -388,9 +376,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int64_t n_rows,
 // later stages (CH + 1 each) and possibly stores, which only raise the
 // count, so vmcnt((R - 1) * (CH + 1)) guarantees stage t has landed.
 
-template <int D>
+template <int D, int NR>
 struct Fp8Ring {
-    static constexpr int R = 3;                       // stages in flight per wave
+    static constexpr int R = NR;                      // ring stages per wave
     static constexpr int CH = D / 32;                 // 16-byte chunks per lane and key
     static constexpr int STAGE = CH * 1024 + 256;     // chunk slabs + per-lane scales
     static constexpr int WAVE = R * STAGE;
@@ -438,14 +426,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, int MB, bool BLOCKS, bool FUSE = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_fp8_kernel(ScoreArgs a, int64_t n_rows,
-                                                        int32_t seg_slots) {
+// NW waves per workgroup, NR ring stages per wave (every launch takes four
+// waves with three stages: two workgroups per CU).
+template <int D, int MB, bool BLOCKS, bool FUSE = false, int NW = 4, int NR = 3>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_fp8_kernel(
+    ScoreArgs a, int64_t n_rows, int32_t seg_slots) {
     static_assert(!FUSE || !BLOCKS, "fused mode: contiguous row segments");
-    using RG = Fp8Ring<D>;
+    constexpr int NT = NW * 64;
+    constexpr int SB = NW * 32;  // slots per sub-block round of the workgroup
+    using RG = Fp8Ring<D, NR>;
     if (FUSE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.fuse_clear = 0;
     constexpr int KS = D / 16;
-    __shared__ __align__(16) uint8_t ring[4 * RG::WAVE];
+    __shared__ __align__(16) uint8_t ring[NW * RG::WAVE];
     // the row's q, zero-padded heads; rows padded by 16 bytes so that the
     // fragment reads (32 head rows, one column) spread over the banks
     constexpr int QS = D + 8;
@@ -454,6 +446,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     constexpr int QN = FUSE && MB * 32 * QS < 2 * kFusedSeg ? 2 * kFusedSeg : MB * 32 * QS;
     __shared__ __align__(16) uint16_t s_q[QN];
     uint32_t* stash = reinterpret_cast<uint32_t*>(s_q);
+    __shared__ uint32_t s_fscr[FUSE ? NT + 32 : 1];
+    uint32_t f_lo = 0xFFFFFFFFu, f_hi = 0u;  // fused mode: range of this lane's valid keys
     __shared__ float s_w[MB * 32];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -482,7 +476,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     if constexpr (BLOCKS) {
         const int32_t* blk_row = a.blk + (a.rows.y0 + y) * a.blk_stride;
         const int32_t n_ent = (a.n_cols + bmask) >> a.block_shift;
-        for (int i = threadIdx.x; i < n_ent; i += 256) s_blk[i] = blk_row[i];
+        for (int i = threadIdx.x; i < n_ent; i += NT) s_blk[i] = blk_row[i];
         __syncthreads();
     }
     auto key_of = [&](int32_t slot, bool& valid) -> int32_t {
@@ -499,9 +493,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
     uint8_t* wring = ring + wave * RG::WAVE;
     const uint32_t wring_addr = (uint32_t)(uintptr_t)wring;
-    // sub-block u of this wave covers slots first + u * 128 .. + 31
+    // sub-block u of this wave covers slots first + u * SB .. + 31
     const int32_t first = slot_begin + wave * 32;
-    const int32_t nsub = first < work_end ? (work_end - first + 127) / 128 : 0;
+    const int32_t nsub = first < work_end ? (work_end - first + SB - 1) / SB : 0;
 
     // D = 128: copy instruction c reads key rows 8c .. 8c+7 of the sub-block
     // as one contiguous KiB (full cache lines, nontemporal): lane j = 8r + q
@@ -516,21 +510,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
             for (int c = 0; c < RG::CH; ++c) {
                 bool valid;
-                const int32_t key = key_of(first + u * 128 + 8 * c + rr, valid);
-                const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+                const int32_t key = key_of(first + u * SB + 8 * c + rr, valid);
+                const int64_t row = kseq + (valid && first + u * SB < work_end ? key : 0);
                 const int chunk = (qq - rr - c) & 7;
                 __builtin_amdgcn_global_load_lds(
                     reinterpret_cast<const uint8_t*>(a.k) + row * D + chunk * 16, st + c * 1024,
                     16, 0, 2);
             }
             bool valid;
-            const int32_t key = key_of(first + u * 128 + m, valid);
-            const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+            const int32_t key = key_of(first + u * SB + m, valid);
+            const int64_t row = kseq + (valid && first + u * SB < work_end ? key : 0);
             __builtin_amdgcn_global_load_lds(a.k_scale + row, st + RG::CH * 1024, 4, 0, 0);
         } else {
             bool valid;
-            const int32_t key = key_of(first + u * 128 + m, valid);
-            const int64_t row = kseq + (valid && first + u * 128 < work_end ? key : 0);
+            const int32_t key = key_of(first + u * SB + m, valid);
+            const int64_t row = kseq + (valid && first + u * SB < work_end ? key : 0);
             const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k) + row * D + hf * (D / 2);
 #pragma unroll
             for (int c = 0; c < RG::CH; ++c)
@@ -587,12 +581,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
             for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
         sc += __shfl_xor(sc, 32);
         sc *= scale;
-        const int32_t j = first + u * 128;
+        const int32_t j = first + u * SB;
         bool valid;
         key_of(j + m, valid);
         const int32_t slot = j + m;
         if constexpr (FUSE) {
-            if (hf == 0 && slot < slot_end) stash[slot - slot_begin] = valid ? score_key(sc) : 0u;
+            const uint32_t key = valid ? score_key(sc) : 0u;
+            // (the second half reuses the stash after the first is filtered)
+            if (hf == 0 && slot < slot_end) stash[(slot - slot_begin) & (kFusedSeg - 1)] = key;
+            if (valid) {
+                f_lo = min(f_lo, key);
+                f_hi = max(f_hi, key);
+            }
         } else if (hf == 0 && slot < slot_end) {
             if (valid)
                 a.out[y * a.out_stride + slot] = sc;
@@ -608,12 +608,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     {
         const int hq = a.heads * D;  // bf16 elements of the row's q
         const uint16_t* qsrc = a.q + qr * hq;
-        for (int e = threadIdx.x * 8; e < MB * 32 * D; e += 256 * 8) {
+        for (int e = threadIdx.x * 8; e < MB * 32 * D; e += NT * 8) {
             u32x4 v = u32x4{0, 0, 0, 0};
             if (e < hq) v = *reinterpret_cast<const u32x4*>(qsrc + e);
             *reinterpret_cast<u32x4*>(&s_q[(e / D) * QS + e % D]) = v;
         }
-        for (int h = threadIdx.x; h < MB * 32; h += 256) s_w[h] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+        for (int h = threadIdx.x; h < MB * 32; h += NT) s_w[h] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -635,23 +635,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     // VALU epilogue of sub-block u, so the matrix and vector pipes overlap
     f32x16 acc0[MB], acc1[MB];
     float sc0 = 1.0f, sc1 = 1.0f;
-    if (nsub > 0) mfma_stage(0, acc0, sc0);
-    for (int32_t u = 0; u < nsub; u += 2) {
-        if (u + 1 < nsub) mfma_stage(u + 1, acc1, sc1);
-        epilogue(u, acc0, sc0);
-        if (u + 1 >= nsub) break;
-        if (u + 2 < nsub) mfma_stage(u + 2, acc0, sc0);
-        epilogue(u + 1, acc1, sc1);
-    }
-    // drain the copies still in flight before the wave's LDS is released
-    wait_vmcnt<0>();
-    if constexpr (FUSE) {
-        // every wave's copies have landed: the ring is the filter's scratch
-        static_assert(4 * RG::WAVE >= kFilterScratch * 4, "filter scratch fits the ring");
-        __syncthreads();
-        const int32_t n_fill = min(slot_end, work_end) - slot_begin;
-        fused_filter<256>(stash, n_fill, limit - slot_begin, a.col_key0 + slot_begin,
-                          reinterpret_cast<uint32_t*>(ring), a.fuse, y, blockIdx.y);
+    auto run = [&](int32_t u0, int32_t u1) {  // this wave's sub-blocks [u0, u1)
+        if (u0 >= u1) return;
+        mfma_stage(u0, acc0, sc0);
+        for (int32_t u = u0; u < u1; u += 2) {
+            if (u + 1 < u1) mfma_stage(u + 1, acc1, sc1);
+            epilogue(u, acc0, sc0);
+            if (u + 1 >= u1) break;
+            if (u + 2 < u1) mfma_stage(u + 2, acc0, sc0);
+            epilogue(u + 1, acc1, sc1);
+        }
+    };
+    if constexpr (!FUSE) {
+        run(0, nsub);
+        // drain the copies still in flight before the wave's LDS is released
+        wait_vmcnt<0>();
+    } else {
+        // fused mode: the segment is parts of kFusedSeg keys (one pool
+        // segment each; sub-blocks [p * kPart, (p + 1) * kPart) of every
+        // wave hold part p).  A part is filtered while the ring copies of
+        // the next part's first stages are in flight; the filter scratch is
+        // its own LDS.
+        constexpr int32_t kPart = kFusedSeg / SB;
+        static_assert(kPart * SB == kFusedSeg, "whole sub-block rounds per part");
+        const int32_t parts = seg_slots / kFusedSeg;
+        for (int32_t p = 0; p < parts; ++p) {
+            const int32_t h = slot_begin + p * kFusedSeg;  // (uniform)
+            if (h >= work_end) break;
+            if (p > 0) {
+                f_lo = 0xFFFFFFFFu;
+                f_hi = 0u;
+                // the stage waits count on copies completing in issue
+                // order; the filter's stores could complete out of order
+                // with them, so a later part starts with nothing in flight
+                // (its first stages have been landing during the filter)
+                wait_vmcnt<0>();
+                __syncthreads();  // (and the filter has read the stash)
+            }
+            run(p * kPart, min(nsub, (p + 1) * kPart));
+            __syncthreads();
+            fused_filter<NT>(stash, min(min(slot_end, work_end) - h, kFusedSeg), min(limit - h, kFusedSeg), a.col_key0 + h,
+                             s_fscr, a.fuse, y, (int32_t)blockIdx.y * parts + p, f_lo, f_hi);
+        }
+        wait_vmcnt<0>();
     }
 }
 
@@ -966,13 +992,20 @@ hipError_t launch_score_fused(const ScoreArgs& a, int64_t n_rows, int32_t n_seg,
     if (n_seg > 65535 || a.fuse.cand == nullptr) return hipErrorInvalidValue;
     // heads padded to 64 (zero q rows and weights add exactly nothing), so
     // the finish's rescoring uses the same instruction sequence
-    const dim3 grid((unsigned)n_rows, (unsigned)n_seg);
-    if (fp8)
-        hipLaunchKernelGGL((score_fp8_kernel<128, 2, false, true>), grid, dim3(256), 0, stream, a,
-                           n_rows, (int32_t)kFusedSeg);
-    else
-        hipLaunchKernelGGL((score_kernel<128, 2, false, false, false, true>), grid, dim3(256), 0,
-                           stream, a, n_rows, (int32_t)kFusedSeg);
+    if (fp8) {
+        // four-wave workgroups, two per CU, each taking two pool segments of
+        // a row (one when that would leave fewer workgroups than CU slots).
+        // (Eight-wave workgroups with four ring stages, one per CU, measured
+        // slower: every part boundary stalls the CU's only workgroup.)
+        const int32_t parts = n_rows * ((n_seg + 1) / 2) >= 512 ? 2 : 1;
+        hipLaunchKernelGGL((score_fp8_kernel<128, 2, false, true, 4, 3>),
+                           dim3((unsigned)n_rows, (unsigned)((n_seg + parts - 1) / parts)), dim3(256), 0,
+                           stream, a, n_rows, (int32_t)(parts * kFusedSeg));
+    } else {
+        hipLaunchKernelGGL((score_kernel<128, 2, false, false, false, true>),
+                           dim3((unsigned)n_rows, (unsigned)n_seg), dim3(256), 0, stream, a, n_rows,
+                           (int32_t)kFusedSeg);
+    }
     return hipGetLastError();
 }
 

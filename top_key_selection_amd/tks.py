@@ -49,7 +49,8 @@ class Shape:
 
 
 SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat_workspace",
-           "tks_topk_flat", "tks_topk_flat_redone", "tks_topk_scores_workspace", "tks_topk_scores",
+           "tks_topk_flat", "tks_topk_flat_redone",
+           "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
            "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_kv_append",
            "tks_gather_selected", "tks_sparse_attention_workspace", "tks_sparse_attention",
