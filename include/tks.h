@@ -131,6 +131,24 @@ int tks_topk_flat(const tks_shape* shape, const void* q, const float* w, const v
                   hipStream_t stream);
 
 /*
+ * tks_topk_flat without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a static
+ * device array of TKS_STATIC_SCRATCH_BYTES in the library, one per GPU,
+ * held until the process ends (its address is looked up on a device's
+ * first call).  A call whose workspace (tks_topk_flat_workspace) exceeds
+ * it returns TKS_EWORKSPACE before anything is launched.  Nothing is
+ * allocated.  Every call on a GPU uses that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must not be
+ * issued; calls on one stream are ordered.  Counters the kernels need at
+ * zero are cleared by the kernels themselves.  Outputs as tks_topk_flat.
+ */
+#define TKS_STATIC_SCRATCH_BYTES (16u << 20)
+int tks_topk_flat_static(const tks_shape* shape, const void* q, const float* w, const void* k,
+                         const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                         int32_t* idx, float* vals, hipStream_t stream);
+
+/*
  * Diagnostic of the fused form: *n_redone (host pointer) receives how many
  * rows of the last tks_topk_flat call that used `workspace` with the same
  * (shape, topk, q_chunk, k_tile) took the exact rescoring path; 0 for the

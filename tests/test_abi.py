@@ -120,6 +120,17 @@ def test_fused_decode_plan_holds_survivors_not_scores():
     assert tks.topk_flat_workspace(s, 2048, 64, 16384) == 64 * 16384 * 4 + 2 * 64 * 2048 * 4
 
 
+def test_static_scratch_entry_refuses_an_oversized_plan_before_any_gpu_call():
+    """tks_topk_flat_static checks its plan against the static scratch
+    before touching a device (this runs without a GPU)."""
+    s = S(n_q=8192, n_k=8192, heads=4, dim=32)
+    assert tks.topk_flat_workspace(tks.Shape(1, 8192, 8192, 4, 32), 2048) > tks.STATIC_SCRATCH_BYTES
+    rc = tks.lib().tks_topk_flat_static(ctypes.byref(s), A, A, A, None, 2048, 0, 0, A, None, None)
+    assert rc == EWS and "static scratch" in tks.last_error()
+    assert tks.lib().tks_topk_flat_static(ctypes.byref(S(dim=48)), A, A, A, None, 4, 0, 0, A, None,
+                                          None) == EUNSUP
+
+
 def test_materialized_score_size_matches_pages():
     # StreamIndex abstract: [B,S,H_I,T] fp32 at S=65,536, H_I=64, T=S/4 is 256 GB
     assert tks.materialized_score_bytes(1, 65536, 64, 65536 // 4) == 2 ** 38

@@ -451,6 +451,61 @@ int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void*
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+
+// The allocation-free flat top-k keeps its workspace in this device array,
+// one per GPU, held until the process ends.  In host code the name is only
+// a stand-in: the array's device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever passed on.
+constexpr size_t kStaticScratchBytes = (size_t)TKS_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// device's first call, with that device current).
+int static_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(TKS_EUNSUPPORTED, "device %d (supported 0..%d)", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || !aligned(ptr, 256)) return fail(TKS_EHIP, "scratch array has no usable device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TKS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tks_topk_flat_static(const tks_shape* s, const void* q, const float* w, const void* k,
+                         const float* k_scale, int32_t topk, int32_t q_chunk, int32_t k_tile,
+                         int32_t* idx, float* vals, hipStream_t stream) {
+    int64_t rows = 0;
+    FlatPlan p{};
+    int rc = flat_checks(s, q, w, k, k_scale, topk, q_chunk, k_tile, idx, vals, &rows, &p);
+    if (rc || rows == 0) return rc;
+    if (p.bytes > kStaticScratchBytes)
+        return fail(TKS_EWORKSPACE,
+                    "the call needs %zu bytes of workspace; the static scratch holds %zu "
+                    "(use tks_topk_flat with a caller workspace)",
+                    p.bytes, kStaticScratchBytes);
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws))) return rc;
+    return topk_flat_run(s, q, w, k, k_scale, topk, idx, vals, p, static_cast<char*>(ws), stream);
+}
+
 int tks_topk_flat_redone(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_tile,
                          const void* workspace, int32_t* n_redone, hipStream_t stream) {
     int rc = check_shape(s, true);

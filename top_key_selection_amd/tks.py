@@ -49,7 +49,7 @@ class Shape:
 
 
 SYMBOLS = ("tks_version", "tks_last_error", "tks_indexer_scores", "tks_topk_flat_workspace",
-           "tks_topk_flat", "tks_topk_flat_redone",
+           "tks_topk_flat", "tks_topk_flat_static", "tks_topk_flat_redone",
            "tks_topk_scores_workspace", "tks_topk_scores",
            "tks_hisa_pool_keys", "tks_hisa_block_select_workspace", "tks_hisa_block_select",
            "tks_hisa_refine_workspace", "tks_hisa_refine_topk", "tks_kv_append",
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.tks_topk_flat_workspace.restype = sz
     L.tks_topk_flat.argtypes = [SP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
     L.tks_topk_flat_redone.argtypes = [SP, i32, i32, i32, P, P, P]
+    L.tks_topk_flat_static.argtypes = [SP, P, P, P, P, i32, i32, i32, P, P, P]
     L.tks_topk_scores_workspace.argtypes = [i32, i32, i32]
     L.tks_topk_scores_workspace.restype = sz
     L.tks_topk_scores.argtypes = [P, i32, i32, i64, P, i32, P, P, P, sz, P]
@@ -96,7 +97,7 @@ def lib() -> ctypes.CDLL:
     L.tks_profile_enable.argtypes = [ctypes.c_int]
     L.tks_profile_read.argtypes = [ctypes.c_char_p, P, P]
     for s in L.tks_profile_enable, L.tks_profile_read, L.tks_indexer_scores, L.tks_topk_flat, \
-            L.tks_topk_flat_redone, L.tks_topk_scores, L.tks_hisa_pool_keys, \
+            L.tks_topk_flat_redone, L.tks_topk_flat_static, L.tks_topk_scores, L.tks_hisa_pool_keys, \
             L.tks_hisa_block_select, L.tks_hisa_refine_topk, L.tks_kv_append, L.tks_gather_selected, \
             L.tks_sparse_attention:
         s.restype = ctypes.c_int
@@ -222,6 +223,26 @@ def topk_flat(shape: Shape, q, w, k, k_scale, topk, q_chunk=0, k_tile=0, with_va
     S = shape.c()
     _check(lib().tks_topk_flat(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), topk, q_chunk,
                                k_tile, _p(idx), _p(vals), _p(ws), _nbytes(ws), _stream()))
+    return idx, vals
+
+
+STATIC_SCRATCH_BYTES = 16 << 20  # TKS_STATIC_SCRATCH_BYTES
+
+
+def topk_flat_static(shape: Shape, q, w, k, k_scale, topk, q_chunk=0, k_tile=0, with_vals=True,
+                     idx=None, vals=None):
+    """topk_flat with the library's static device scratch instead of a
+    workspace (nothing is allocated by the library; outputs are allocated
+    here unless given).  Calls that overlap on one GPU must not be issued."""
+    _qwk(shape, q, w, k, k_scale)
+    dev = q.device
+    n_out = shape.batch * shape.n_q * topk
+    idx = _out(idx, "idx", n_out, torch.int32, (shape.batch, shape.n_q, topk), dev)
+    if vals is not None or with_vals:
+        vals = _out(vals, "vals", n_out, torch.float32, (shape.batch, shape.n_q, topk), dev)
+    S = shape.c()
+    _check(lib().tks_topk_flat_static(ctypes.byref(S), _p(q), _p(w), _p(k), _p(k_scale), topk,
+                                      q_chunk, k_tile, _p(idx), _p(vals), _stream()))
     return idx, vals
 
 
