@@ -20,6 +20,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tks_oracle.c")
 _LIB = os.path.join(_HERE, "libtks_oracle.so")
+# TKS_ORACLE_LIB: an oracle built elsewhere (the sanitizer check's build)
+_LIB_OVERRIDE = os.environ.get("TKS_ORACLE_LIB")
 
 FORCE_FIRST = 1
 FORCE_LOCAL = 2
@@ -40,15 +42,32 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (ROCm's clang, whose runtime also serves the sanitized library build; no
+    OpenMP) into out_dir.  Returns the library path."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libtks_oracle.so")
+    if not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        subprocess.check_call(["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+                               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                               "-std=gnu11", "-fPIC", "-shared", "-Wall", "-Wextra", _SRC, "-o",
+                               out, "-lm"])
+    return out
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, u32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
         SP = ctypes.POINTER(_Shape)

@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtks.so")
+# TKS_LIB overrides the library file (the sanitizer check loads a host-only,
+# AddressSanitizer-instrumented build of the same sources through it)
+LIB_PATH = os.environ.get("TKS_LIB") or os.path.join(_HERE, "libtks.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 KEY_BF16, KEY_FP8_E4M3FN = 0, 1
