@@ -251,6 +251,38 @@ def test_shared_key_hisa_prefill_exact():
                       "shared hisa")
 
 
+def test_shared_key_refine_ring_refills_exact():
+    """HISA prefill long enough that each workgroup's key segment holds more
+    ring stages than the ring has slots, so slots are refilled while other
+    rows of the workgroup still compute: two sequences, every row keeping a
+    different block list, one call over all rows and one whose query chunk
+    straddles the sequences.  Sampled rows (wave, chunk and sequence
+    boundaries) must equal the oracle's blocks and tokens exactly."""
+    say("HISA refine ring refills: 2 x 1024 queries, 32768 keys")
+    batch, n_q, n_k, heads = 2, 1024, 32768, 64
+    block, m_scored, topk = 64, 16, 512
+    flags = FORCE_FIRST | FORCE_LOCAL
+    sh, x = int_case(77, batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=128,
+                     q_pos0=n_k - n_q, lo=-2, hi=2)
+    R = batch * n_q
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 7, 8, 15, 1023, 1024, 1031, 1535, 1536, 2047],
+                                     rng.choice(R, 54, replace=False)]))
+    qr = x["q"].reshape(R, heads, 128)[rows]
+    wr = x["w"].reshape(R, heads)[rows]
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, block, m_scored, flags, topk, rows)
+    S = tks.Shape(**sh)
+    q, w, k, ks = gpu_inputs(x)
+    pooled = tks.hisa_pool_keys(S, k, ks, block)
+    blk, _ = tks.hisa_block_select(S, q, w, pooled, block, m_scored, flags, with_vals=False)
+    for q_chunk in (0, 1536):
+        idx, vals = tks.hisa_refine_topk(S, q, w, k, ks, block, blk, topk, q_chunk)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(blk).reshape(R, -1)[rows], blk_o)
+        assert_topk_exact(host(idx).reshape(R, -1)[rows], host(vals).reshape(R, -1)[rows], idx_o,
+                          val_o, "ring refills q_chunk=%d" % q_chunk)
+
+
 def test_tied_running_list_across_tiles_keeps_lowest_indices():
     """Scores tied at the k-th place across key tiles: the running list of
     earlier tiles carries the tie group, and the later tiles' selection must

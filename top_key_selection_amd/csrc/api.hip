@@ -753,6 +753,7 @@ struct RefinePlan {
     int32_t slots;
     int32_t chunk;
     int64_t stride;
+    bool shared;        // prefill rows, bf16 keys, dim 128: the shared-key ring
     size_t bytes;
 };
 
@@ -761,6 +762,7 @@ RefinePlan plan_refine(const tks_shape* s, int32_t block, int32_t m_total, int32
     p.rows = (int64_t)s->batch * s->n_q;
     p.slots = block * m_total;
     p.stride = round_up(p.slots, 4);
+    p.shared = s->key_dtype == TKS_KEY_BF16 && s->dim == 128 && s->n_q > 1;
     int64_t c = q_chunk > 0 ? q_chunk : kScoreBudget / (p.stride * 4);
     p.chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, std::max<int64_t>(p.rows, 1)));
     p.bytes = round_up((int64_t)p.chunk * p.stride * 4, 256);
@@ -826,7 +828,14 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
         hipError_t e;
         {
             Timed tm("score_refine", stream);
-            e = tks::launch_score(a, n, s->dim, fp8, true, stream);
+            if (p.shared) {
+                // keys of the run: up to the last visible key of the chunk
+                a.n_cols = max_visible(s, g0, g0 + n);
+                a.col_key0 = 0;
+                e = tks::launch_score_refine_shared(a, n, stream);
+            } else {
+                e = tks::launch_score(a, n, s->dim, fp8, true, stream);
+            }
         }
         if (e != hipSuccess) return hip_fail(e, "refine score launch");
 

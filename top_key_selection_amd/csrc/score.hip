@@ -18,6 +18,7 @@
 //   * fp8 e4m3fn keys are widened exactly to bf16 in registers
 //     (v_cvt_scalef32_pk_bf16_fp8, scale 1) and the per-token scale is applied
 //     to the reduced score (scale >= 0 commutes with the ReLU).
+
 #include <algorithm>
 
 #include "score_common.hpp"
@@ -924,6 +925,254 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
     wait_vmcnt<0>();
 }
 
+// ------------------------------------------------------------------------
+// HISA refinement for prefill (HISA abstract: the token indexer again, only
+// inside each query's kept blocks).  Neighbouring queries keep nearly
+// disjoint block sets (sixteen neighbours together keep nearly every visible
+// block), so no key is shared by many queries' block lists; the keys are
+// shared by position instead.  The workgroup is the shared-key one: NW
+// consecutive query rows, one per wave, and the same LDS ring streaming a
+// run of keys for all of them.  A wave runs the MFMAs and head reduction of
+// a 32-key sub-block only when its row kept the sub-block's block, found by
+// walking the row's ascending block list alongside the keys, and writes the
+// scores to the row's slots e * B + (key mod B) for list entry e.  The
+// arithmetic is the flat kernel's, so the scores are the same fp32 values.
+// Refinement over a shared key ring with producer and consumer waves.
+// NW consumer waves (one query row each) walk the ring at their own pace:
+// a wave skips the sub-blocks its row did not keep and may run up to NS - 1
+// stages ahead of the slowest, so the rows' different block lists average
+// out instead of every stage costing the slowest row's work (as it would
+// with a barrier per stage).  NP producer waves only copy, each whole
+// stages in turn: a producer waits until every consumer is done with the
+// stage its slot held, copies the new one, waits for its own loads and
+// publishes it, so NP stages are in flight at once.  Each slot counts the
+// consumers done with it over all its stages (the stage in slot x % NS may
+// be overwritten by stage x once the count reaches NW * (x / NS)), and holds
+// the number of the stage it has.  Waits are sleep loops: a consumer waits
+// only for a producer, which waits only for consumers finishing an earlier
+// stage, so every loop ends; the bound keeps a kernel from hanging forever
+// should that reasoning fail.
+constexpr int32_t kRingSpinMax = 1 << 22;
+
+template <typename F>
+__device__ __forceinline__ void spin_until(F&& ok) {
+    for (int32_t spin = 0; spin < kRingSpinMax; ++spin) {
+        if (ok()) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// NW rows per workgroup, NS ring stages of 128 keys (32 KiB), NP producers.
+template <int MB, int NW, int NS, int NP>
+__global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs a, int64_t n_rows,
+                                                                       int32_t blocks_per_seq,
+                                                                       int32_t seg_slots) {
+    using RG = SharedRing;
+    constexpr int D = RG::D;
+    constexpr int KS = D / 16;
+    constexpr int PIECES = RG::STAGE / (64 * 16);   // 16-byte copies of a stage per lane
+    constexpr int CPW = PIECES / NW;                // ... per consumer in the first stages
+    static_assert(CPW * NW == PIECES, "stage split");
+    static_assert(NS > NP && NP >= 1, "ring depth");
+    __shared__ __align__(16) uint8_t ring[NS * RG::STAGE];
+    __shared__ int32_t s_ready[NS];                 // stage held by each slot
+    __shared__ int32_t s_done[NS];                  // consumers done, all stages of the slot
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int hf = lane >> 5;
+
+    // chunk rows [r_lo, r_hi) of one sequence (as in score_shared_kernel)
+    const int64_t R = a.rows.rows_per_seq;
+    const int64_t seq = a.rows.y0 / R + blockIdx.x / blocks_per_seq;
+    const int64_t s_lo = seq * R - a.rows.y0;
+    const int64_t lo = s_lo > 0 ? s_lo : 0;
+    const int64_t hi = s_lo + R < n_rows ? s_lo + R : n_rows;
+    const int64_t r_lo = lo + (int64_t)(blockIdx.x % blocks_per_seq) * NW;
+    if (r_lo >= hi) return;
+    const int64_t r_hi = r_lo + NW < hi ? r_lo + NW : hi;
+    const bool consumer = wave < NW;
+    const bool active = consumer && r_lo + wave < r_hi;
+    const int64_t y = active ? r_lo + wave : r_hi - 1;
+    const int32_t t = a.rows.t_begin + (int32_t)(y - s_lo);
+    const int64_t qr = seq * a.rows.n_q + t;
+    const int32_t n_tok = a.vis.tokens(t);
+
+    const int32_t slot_begin = blockIdx.y * seg_slots;  // key slots (key = slot)
+    const int32_t work_end =
+        min(min(a.n_cols, slot_begin + seg_slots), a.vis.tokens(a.rows.t_begin + (int32_t)(r_hi - 1 - s_lo)));
+    if (slot_begin >= work_end) return;
+    const int32_t n_st = (work_end - slot_begin + RG::SK - 1) / RG::SK;
+    const int32_t nsub = (work_end - slot_begin + 31) / 32;
+
+    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k) + seq * a.k_seq_len * (2 * D);
+    const int32_t kmax = (int32_t)(a.k_seq_len - 1);
+    // piece p (16 bytes at slot offset 16 p) of a stage is key row p / 16,
+    // physical chunk p % 16, logical chunk (p % 16) ^ (row % 16); p - lane is
+    // the same for the whole wave (the copy's LDS base)
+    auto copy_piece = [&](uint8_t* sp, int32_t key0, int p) {
+        const int32_t key = min(key0 + (p >> 4), kmax);
+        const uint32_t chunk = (uint32_t)(((p & 15) ^ ((p >> 4) & 15)) * 16);
+        __builtin_amdgcn_global_load_lds(kseq + ((int64_t)key * (2 * D) + (int64_t)chunk),
+                                         sp + (p - lane) * 16, 16, 0, 0);
+    };
+
+    // the row's kept blocks of the segment as a mask (bit i: block b0 + i; a
+    // segment starts on a block boundary and spans at most 64 blocks) and
+    // the list position of the first of them (the list is ascending)
+    const int32_t bshift = a.block_shift;
+    const int32_t b0 = slot_begin >> bshift;
+    uint32_t kmask_lo = 0, kmask_hi = 0;
+    int32_t before = 0;
+    if (active) {
+        const int32_t* lst = a.blk + (a.rows.y0 + y) * a.blk_stride;
+        for (int i = lane; i < a.blk_stride; i += 64) {
+            const int32_t e = lst[i];
+            if (e >= 0 && e < b0) {
+                ++before;
+            } else if (e >= b0 && e < b0 + 64) {
+                if (e - b0 < 32)
+                    kmask_lo |= 1u << (e - b0);
+                else
+                    kmask_hi |= 1u << (e - b0 - 32);
+            }
+        }
+    }
+    // first NS stages: copied by the consumers together
+    if (consumer) {
+#pragma unroll 1
+        for (int st = 0; st < NS; ++st) {
+            if (st < n_st) {
+                uint8_t* sp = ring + st * RG::STAGE;
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) copy_piece(sp, slot_begin + st * RG::SK, (i * NW + wave) * 64 + lane);
+            }
+        }
+    }
+    if (threadIdx.x < NS) {
+        s_ready[threadIdx.x] = threadIdx.x < n_st ? (int32_t)threadIdx.x : -1;
+        s_done[threadIdx.x] = 0;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // the first stages and the slot states
+
+    if (!consumer) {
+#pragma unroll 1
+        for (int32_t x = NS + (wave - NW); x < n_st; x += NP) {
+            const int sl = x % NS;
+            const int32_t freed = NW * (x / NS);
+            spin_until([&] {
+                return __hip_atomic_load(&s_done[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= freed;
+            });
+            uint8_t* sp = ring + sl * RG::STAGE;
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) copy_piece(sp, slot_begin + x * RG::SK, i * 64 + lane);
+            wait_vmcnt<0>();
+            if (lane == 0) __hip_atomic_store(&s_ready[sl], x, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        return;
+    }
+
+    bf16x8 qa[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int h = mb * 32 + m;
+        if (h < a.heads) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(a.q + (qr * a.heads + h) * D + hf * (D / 2));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, p[ks]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        }
+    }
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int h = mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
+            wv[mb][j] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+        }
+    uint32_t roff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = m * (2 * D) + (((hf * 8 + ks) ^ (m & 15)) * 16);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmask_lo |= __shfl_xor(kmask_lo, o);
+        kmask_hi |= __shfl_xor(kmask_hi, o);
+        before += __shfl_xor(before, o);
+    }
+    const uint64_t kmask = ((uint64_t)__builtin_amdgcn_readfirstlane(kmask_hi) << 32) |
+                           (uint64_t)__builtin_amdgcn_readfirstlane(kmask_lo);
+    before = __builtin_amdgcn_readfirstlane(before);
+    const int32_t bmask = (1 << bshift) - 1;
+    float* orow = a.out + y * a.out_stride;
+
+#pragma unroll 1
+    for (int32_t st = 0; st < n_st; ++st) {
+        const int slot = st % NS;
+        // every stage is waited for, also one this row skips: a wave is then
+        // never more than NS - 1 stages ahead of the slowest, which is what
+        // makes the slot counts exact
+        spin_until([&] {
+            return __hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == st;
+        });
+        const uint8_t* sb = ring + slot * RG::STAGE;
+#pragma unroll
+        for (int j = 0; j < RG::SPS; ++j) {
+            const int32_t u = st * RG::SPS + j;
+            if (u >= nsub) break;
+            const int32_t key0 = slot_begin + u * 32;
+            const int32_t bi = (key0 >> bshift) - b0;  // 0 .. 63
+            if (!((kmask >> bi) & 1) || key0 >= n_tok) continue;
+            const int32_t ptr = before + __builtin_popcountll(kmask & ((1ull << bi) - 1));
+            f32x16 acc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kb = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(sb + j * 32 * (2 * D) + roff[ks]));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+            }
+            float sc = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
+            sc = add_upper_half(sc);
+            const int32_t key = key0 + m;
+            if (hf == 0 && key < n_tok) orow[ptr * (bmask + 1) + (key & bmask)] = sc;
+        }
+        // done with the slot: its keys were read into registers above
+        if (lane == 0) __hip_atomic_fetch_add(&s_done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+template <int MB, int NW, int NS, int NP>
+hipError_t launch_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
+    const int64_t R = a.rows.rows_per_seq;
+    const int64_t n_seq = (a.rows.y0 + n_rows - 1) / R - a.rows.y0 / R + 1;
+    const int64_t per_seq = (std::min<int64_t>(n_rows, R) + NW - 1) / NW;
+    // segments: whole blocks and whole stages, at most 64 blocks (the
+    // kernel's kept-block mask), sized for a few workgroups per CU (each
+    // computes about a quarter of what a flat one would)
+    const int64_t unit = std::max<int64_t>(SharedRing::SK, int64_t(1) << a.block_shift);
+    const int64_t cap = int64_t(64) << a.block_shift;
+    const int64_t want = n_rows * (int64_t)a.n_cols / (NW * 8192);
+    const int64_t seg = std::min<int64_t>(cap, std::max<int64_t>(2048, (want + unit - 1) / unit * unit));
+    if ((a.n_cols + seg - 1) / seg > 65535) return hipErrorInvalidValue;
+    dim3 grid((unsigned)(n_seq * per_seq), (unsigned)((a.n_cols + seg - 1) / seg));
+    hipLaunchKernelGGL((refine_shared_kernel<MB, NW, NS, NP>), grid, dim3((NW + NP) * 64), 0, stream, a, n_rows,
+                       (int32_t)per_seq, (int32_t)seg);
+    return hipGetLastError();
+}
+
 template <int MB, int NW>
 hipError_t launch_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     const int64_t R = a.rows.rows_per_seq;
@@ -985,6 +1234,12 @@ hipError_t launch_d(const ScoreArgs& a, int64_t n_rows, bool fp8, bool blocks, h
 }
 
 }  // namespace
+
+hipError_t launch_score_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
+    if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
+    return a.heads > 32 ? launch_refine_shared<2, kSharedRows, 4, 3>(a, n_rows, stream)
+                        : launch_refine_shared<1, kSharedRows, 4, 3>(a, n_rows, stream);
+}
 
 hipError_t launch_score_fused(const ScoreArgs& a, int64_t n_rows, int32_t n_seg, bool fp8,
                               hipStream_t stream) {

@@ -174,6 +174,10 @@ size_t select_split_workspace(int64_t n_rows, const SelectSplit& sp);
 hipError_t launch_select_split(const SelectArgs& a, int64_t n_rows, const SelectSplit& sp,
                                void* ws, hipStream_t stream);
 hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
+// HISA refinement scoring of prefill rows (bf16 keys, D = 128; keys shared
+// by position through the shared-key ring; a.n_cols = keys of the run,
+// a.blk / a.blk_stride = block lists, a.out = [rows, blk_stride << shift])
+hipError_t launch_score_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int dim, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int64_t n_rows, hipStream_t stream);
 size_t attend_workspace(int64_t rows, int32_t heads, int32_t topk);
