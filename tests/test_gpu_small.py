@@ -283,6 +283,56 @@ def test_shared_key_refine_ring_refills_exact():
                           val_o, "ring refills q_chunk=%d" % q_chunk)
 
 
+@pytest.mark.parametrize("block,m_scored,n_k,q_chunk", [(32, 12, 3001, 70), (256, 5, 5000, 0),
+                                                         (64, 8, 4100, 33), (128, 3, 700, 0)])
+def test_scheduled_refine_block_sizes_exact(block, m_scored, n_k, q_chunk):
+    """Prefill refinement with a plan per group of 8 rows (bf16 keys, D = 128):
+    32-key blocks put four plan positions in one 128-key ring stage, 256-key
+    blocks spread one position over two stages; ragged caches, a query chunk
+    that splits sequences and groups, rows with fewer than 8 in their group.
+    Blocks and tokens must equal the oracle's."""
+    say("scheduled refine B=%d m=%d n_k=%d q_chunk=%d" % (block, m_scored, n_k, q_chunk))
+    batch, n_q, heads = 2, 100, 64
+    flags = FORCE_FIRST | FORCE_LOCAL
+    sh, x = int_case(40 + block, batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=128,
+                     q_pos0=n_k - n_q, lo=-2, hi=2)
+    R = batch * n_q
+    rows = np.arange(R)
+    qr, wr = x["q"].reshape(R, heads, 128), x["w"].reshape(R, heads)
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, block, m_scored, flags, 300, rows)
+    S = tks.Shape(**sh)
+    q, w, k, ks = gpu_inputs(x)
+    pooled = tks.hisa_pool_keys(S, k, ks, block)
+    blk, _ = tks.hisa_block_select(S, q, w, pooled, block, m_scored, flags, with_vals=False)
+    idx, vals = tks.hisa_refine_topk(S, q, w, k, ks, block, blk, 300, q_chunk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                      "scheduled refine B=%d" % block)
+
+
+def test_refine_lists_too_long_for_a_plan_take_the_segment_ring_exact():
+    """A group's union of kept blocks can exceed what one plan holds (here
+    8 rows x 150 entries over 1250 blocks of 32 keys): such shapes refine
+    through the key-segment ring instead; results must equal the oracle's."""
+    say("refine without a plan: B=32, m_total 150, n_k 40000")
+    batch, n_q, n_k, heads, block, m_scored = 1, 48, 40000, 64, 32, 148
+    flags = FORCE_FIRST | FORCE_LOCAL
+    sh, x = int_case(91, batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=128,
+                     q_pos0=n_k - n_q, lo=-2, hi=2)
+    R = batch * n_q
+    rows = np.arange(R)
+    qr, wr = x["q"].reshape(R, heads, 128), x["w"].reshape(R, heads)
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, block, m_scored, flags, 1024, rows)
+    S = tks.Shape(**sh)
+    q, w, k, ks = gpu_inputs(x)
+    idx, vals, blk = tks.hisa_topk(S, q, w, k, ks, block, m_scored, flags, 1024)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                      "segment ring refine")
+
+
 def test_tied_running_list_across_tiles_keeps_lowest_indices():
     """Scores tied at the k-th place across key tiles: the running list of
     earlier tiles carries the tie group, and the later tiles' selection must

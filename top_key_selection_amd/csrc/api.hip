@@ -754,6 +754,11 @@ struct RefinePlan {
     int32_t chunk;
     int64_t stride;
     bool shared;        // prefill rows, bf16 keys, dim 128: the shared-key ring
+    bool sched;         // ... with a plan per group of rows (bounded sizes)
+    int32_t sched_stride;
+    int32_t sched_blocks;
+    int64_t groups;     // plan groups of a chunk at most
+    size_t off_n, off_blk, off_rank;  // plan arrays in the workspace
     size_t bytes;
 };
 
@@ -766,6 +771,22 @@ RefinePlan plan_refine(const tks_shape* s, int32_t block, int32_t m_total, int32
     int64_t c = q_chunk > 0 ? q_chunk : kScoreBudget / (p.stride * 4);
     p.chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, std::max<int64_t>(p.rows, 1)));
     p.bytes = round_up((int64_t)p.chunk * p.stride * 4, 256);
+    // the plan of a group holds its union of kept blocks: at most every
+    // block of the cache, and at most every list entry of its rows
+    const int64_t nb_all = ((int64_t)s->n_k + block - 1) / block;
+    const int64_t pu = std::min<int64_t>(nb_all, (int64_t)tks::kSchedRows * m_total);
+    p.sched = p.shared && nb_all >= 1 && nb_all <= tks::kSchedMaxBlocks && pu <= tks::kSchedMaxPos;
+    if (p.sched) {
+        p.sched_stride = (int32_t)round_up(pu, 4);
+        p.sched_blocks = (int32_t)nb_all;
+        const int64_t per_seq = (std::min<int64_t>(p.chunk, s->n_q) + tks::kSchedRows - 1) / tks::kSchedRows;
+        const int64_t n_seq = std::min<int64_t>(s->batch, (p.chunk + s->n_q - 1) / s->n_q + 1);
+        p.groups = n_seq * per_seq;
+        p.off_n = p.bytes;
+        p.off_blk = p.off_n + round_up(p.groups * 4, 256);
+        p.off_rank = p.off_blk + round_up(p.groups * p.sched_stride * 4, 256);
+        p.bytes = p.off_rank + round_up(p.groups * p.sched_stride * tks::kSchedRows * 2, 256);
+    }
     return p;
 }
 
@@ -828,7 +849,16 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
         hipError_t e;
         {
             Timed tm("score_refine", stream);
-            if (p.shared) {
+            if (p.sched) {
+                uint8_t* base = static_cast<uint8_t*>(workspace);
+                a.sched.n_pos = reinterpret_cast<int32_t*>(base + p.off_n);
+                a.sched.blocks = reinterpret_cast<int32_t*>(base + p.off_blk);
+                a.sched.ranks = reinterpret_cast<int16_t*>(base + p.off_rank);
+                a.sched.stride = p.sched_stride;
+                a.sched.max_blocks = p.sched_blocks;
+                e = tks::refine_sched_groups(rm, n) > p.groups ? hipErrorInvalidValue
+                                                                : tks::launch_score_refine_sched(a, n, stream);
+            } else if (p.shared) {
                 // keys of the run: up to the last visible key of the chunk
                 a.n_cols = max_visible(s, g0, g0 + n);
                 a.col_key0 = 0;

@@ -1103,8 +1103,10 @@ __global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs
         kmask_hi |= __shfl_xor(kmask_hi, o);
         before += __shfl_xor(before, o);
     }
-    const uint64_t kmask = ((uint64_t)__builtin_amdgcn_readfirstlane(kmask_hi) << 32) |
-                           (uint64_t)__builtin_amdgcn_readfirstlane(kmask_lo);
+    // (the builtin returns a signed int: widen through uint32_t, or a set bit
+    // 31 of the low word would sign-extend over the high word)
+    const uint64_t kmask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)kmask_hi) << 32) |
+                           (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)kmask_lo);
     before = __builtin_amdgcn_readfirstlane(before);
     const int32_t bmask = (1 << bshift) - 1;
     float* orow = a.out + y * a.out_stride;
@@ -1173,6 +1175,372 @@ hipError_t launch_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t 
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------
+// Scheduled refinement.  In the segment ring above, a workgroup's time is
+// set by the row of its 8 that kept the most blocks of the segment, and
+// rows keep their blocks very unevenly along the keys, though each row
+// keeps the same number in all (the scored blocks plus the forced ones).  So
+// a group of 8 rows takes its whole visible range at once, and a plan orders
+// the blocks any of them kept so that every row's work is spread evenly
+// along the order: then the consumers run at about the same pace and the
+// ring's few stages of slack suffice.  Blocks that no row kept are not
+// copied at all.
+//
+// The plan (one wave per group) is greedy.  Blocks that the same rows kept
+// (the same 8-bit pattern) are interchangeable, so each step picks a pattern:
+// the one whose rows are furthest behind an even pace, score(p) = sum over
+// rows j in p of (s + 1) * n_j / n - done_j, scaled by n to stay integer
+// (n blocks in all, n_j of them kept by row j, done_j scheduled so far);
+// ties go to the smaller pattern, and a pattern's blocks go in ascending
+// order, so the plan is a function of the block lists alone.
+
+struct SchedGroup {
+    int64_t s_lo;  // chunk row of the sequence's first row (may be negative)
+    int64_t r_lo, r_hi;
+    int64_t seq;
+};
+
+__device__ __forceinline__ bool sched_group(const ScoreArgs& a, int64_t n_rows, int32_t per_seq,
+                                            int64_t g, SchedGroup& G) {
+    const int64_t R = a.rows.rows_per_seq;
+    G.seq = a.rows.y0 / R + g / per_seq;
+    G.s_lo = G.seq * R - a.rows.y0;
+    const int64_t lo = G.s_lo > 0 ? G.s_lo : 0;
+    const int64_t hi = G.s_lo + R < n_rows ? G.s_lo + R : n_rows;
+    G.r_lo = lo + (g % per_seq) * kSchedRows;
+    G.r_hi = G.r_lo + kSchedRows < hi ? G.r_lo + kSchedRows : hi;
+    return G.r_lo < hi;
+}
+
+// LDS of the plan kernel for `nb` (a multiple of 64) visible blocks and a
+// layout stride `P`: pattern words, block -> union index, union blocks,
+// union ranks, pattern counts, union patterns
+__host__ __device__ constexpr size_t plan_lds_bytes(int32_t nb, int32_t P) {
+    return 3 * (size_t)nb + 21 * (size_t)P + 1024;
+}
+
+__global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_rows, int32_t per_seq,
+                                                         int32_t lds_blocks) {
+    extern __shared__ __align__(16) uint8_t plan_lds[];
+    const int lane = threadIdx.x;
+    const RefineSched P = a.sched;
+    SchedGroup G;
+    if (!sched_group(a, n_rows, per_seq, blockIdx.x, G)) {
+        if (lane == 0) P.n_pos[blockIdx.x] = 0;
+        return;
+    }
+    const int nr = (int)(G.r_hi - G.r_lo);
+    const int32_t bshift = a.block_shift;
+    const int32_t m_total = a.blk_stride;
+    // blocks with a visible key, per row and for the group
+    int32_t nbv_row[kSchedRows];
+    int32_t nbv = 0;
+#pragma unroll
+    for (int j = 0; j < kSchedRows; ++j) {
+        const int32_t n_tok = j < nr ? a.vis.tokens(a.rows.t_begin + (int32_t)(G.r_lo + j - G.s_lo)) : 0;
+        nbv_row[j] = n_tok > 0 ? min(((n_tok - 1) >> bshift) + 1, lds_blocks) : 0;
+        nbv = max(nbv, nbv_row[j]);
+    }
+    uint32_t* pw = reinterpret_cast<uint32_t*>(plan_lds);                 // [lds_blocks / 4]
+    int16_t* umap = reinterpret_cast<int16_t*>(plan_lds + lds_blocks);    // [lds_blocks]
+    int32_t* ublk = reinterpret_cast<int32_t*>(plan_lds + 3 * (size_t)lds_blocks);  // [P]
+    int16_t* urank = reinterpret_cast<int16_t*>(ublk + P.stride);        // [P, kSchedRows]
+    int32_t* pcnt = reinterpret_cast<int32_t*>(urank + (size_t)P.stride * kSchedRows);  // [256]
+    uint8_t* upat = reinterpret_cast<uint8_t*>(pcnt + 256);              // [P]
+
+    const int nw = (nbv + 3) >> 2;
+    for (int i = lane; i < nw; i += 64) pw[i] = 0u;
+    for (int i = lane; i < 256; i += 64) pcnt[i] = 0;
+    __syncthreads();
+    // patterns: bit j of block b's byte = row j kept b
+    for (int j = 0; j < nr; ++j) {
+        const int32_t* lst = a.blk + (a.rows.y0 + G.r_lo + j) * (int64_t)m_total;
+        for (int i = lane; i < m_total; i += 64) {
+            const int32_t e = lst[i];
+            if (e >= 0 && e < nbv_row[j]) atomicOr(&pw[e >> 2], 1u << (8 * (e & 3) + j));
+        }
+    }
+    __syncthreads();
+    // the union in ascending block order: lane owns words [w0, w1)
+    const int cw = (nw + 63) >> 6;
+    const int w0 = min(nw, lane * cw);
+    const int w1 = min(nw, w0 + cw);
+    int32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t v = pw[w];
+        cnt += ((v & 0xFFu) != 0u) + ((v & 0xFF00u) != 0u) + ((v & 0xFF0000u) != 0u) + ((v >> 24) != 0u);
+    }
+    int32_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    const int32_t n_u = __shfl(inc, 63);  // <= min(nbv, nr * m_total) <= P.stride
+    int32_t u = inc - cnt;
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t v = pw[w];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t pat = (v >> (8 * b)) & 0xFFu;
+            if (pat != 0u) {
+                ublk[u] = 4 * w + b;
+                upat[u] = (uint8_t)pat;
+                umap[4 * w + b] = (int16_t)u;
+                ++u;
+            }
+        }
+    }
+    for (int i = lane; i < n_u * kSchedRows; i += 64) urank[i] = -1;
+    __syncthreads();
+    int32_t tot[kSchedRows];
+#pragma unroll
+    for (int j = 0; j < kSchedRows; ++j) tot[j] = 0;
+    for (int i = lane; i < n_u; i += 64) {
+        const uint32_t pat = upat[i];
+        atomicAdd(&pcnt[pat], 1);
+#pragma unroll
+        for (int j = 0; j < kSchedRows; ++j) tot[j] += (pat >> j) & 1u;
+    }
+    for (int j = 0; j < nr; ++j) {
+        const int32_t* lst = a.blk + (a.rows.y0 + G.r_lo + j) * (int64_t)m_total;
+        for (int i = lane; i < m_total; i += 64) {
+            const int32_t e = lst[i];
+            if (e >= 0 && e < nbv_row[j]) urank[umap[e] * kSchedRows + j] = (int16_t)i;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kSchedRows; ++j)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) tot[j] += __shfl_xor(tot[j], o);
+    __syncthreads();
+
+    // greedy over patterns: lane owns patterns 4 lane .. 4 lane + 3
+    int32_t T[4], Dn[4], C[4], CUR[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int p = lane * 4 + k;
+        T[k] = 0;
+#pragma unroll
+        for (int j = 0; j < kSchedRows; ++j) T[k] += ((p >> j) & 1) * tot[j];
+        Dn[k] = 0;
+        C[k] = p == 0 ? 0 : pcnt[p];
+        CUR[k] = 0;
+    }
+    int32_t* out_blk = P.blocks + (int64_t)blockIdx.x * P.stride;
+    int16_t* out_rank = P.ranks + (int64_t)blockIdx.x * P.stride * kSchedRows;
+    for (int32_t st = 0; st < n_u; ++st) {
+        int32_t best = INT32_MIN, bp = 256;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int32_t sc = (st + 1) * T[k] - n_u * Dn[k];
+            if (C[k] > 0 && sc > best) {
+                best = sc;
+                bp = lane * 4 + k;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const int32_t ob = __shfl_xor(best, o);
+            const int32_t op = __shfl_xor(bp, o);
+            if (ob > best || (ob == best && op < bp)) {
+                best = ob;
+                bp = op;
+            }
+        }
+        const int32_t ps = __builtin_amdgcn_readfirstlane(bp);  // has blocks left
+        const int owner = ps >> 2;
+        const int ks = ps & 3;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Dn[k] += __builtin_popcount((uint32_t)((lane * 4 + k) & ps));
+        const int32_t my_cur = ks == 0 ? CUR[0] : ks == 1 ? CUR[1] : ks == 2 ? CUR[2] : CUR[3];
+        // the pattern's next block in ascending order, 64 union entries at a time
+        int32_t uu = 0;
+        for (int32_t c = __shfl(my_cur, owner); c < n_u; c += 64) {
+            const int32_t idx = c + lane;
+            const uint64_t hit = __ballot(idx < n_u && upat[idx] == (uint32_t)ps);
+            if (hit != 0ull) {
+                uu = c + __builtin_ctzll(hit);
+                break;
+            }
+        }
+        if (lane == owner) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k == ks) {
+                    CUR[k] = uu + 1;
+                    C[k] -= 1;
+                }
+        }
+        if (lane == 0) out_blk[st] = ublk[uu];
+        if (lane < kSchedRows) out_rank[(int64_t)st * kSchedRows + lane] = urank[uu * kSchedRows + lane];
+    }
+    if (lane == 0) P.n_pos[blockIdx.x] = n_u;
+}
+
+// One workgroup per group: kSchedRows consumer waves (one row each) and NP
+// producer waves over the plan's blocks, through an NS-stage ring of 128 key
+// slots (with blocks of 32 or 64 keys a stage holds several plan positions,
+// with 256-key blocks a position spans two stages).  Producers copy every
+// stage (the first ones too, into free slots) and read a stage's block ids
+// before issuing its copies; consumers issue no copies at all.
+template <int MB, int NS, int NP>
+__global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(ScoreArgs a, int64_t n_rows,
+                                                                            int32_t per_seq) {
+    using RG = SharedRing;
+    constexpr int NW = kSchedRows;
+    constexpr int D = RG::D;
+    constexpr int KS = D / 16;
+    constexpr int PIECES = RG::STAGE / (64 * 16);  // 16-byte copies of a stage per lane
+    static_assert(NS > NP && NP >= 1, "ring depth");
+    __shared__ __align__(16) uint8_t ring[NS * RG::STAGE];
+    __shared__ int32_t s_blk[kSchedMaxPos];
+    __shared__ __align__(16) int16_t s_rank[kSchedMaxPos * NW];
+    __shared__ int32_t s_ready[NS];  // stage held by each slot
+    __shared__ int32_t s_done[NS];   // consumers done, all stages of the slot
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int hf = lane >> 5;
+
+    SchedGroup G;
+    if (!sched_group(a, n_rows, per_seq, blockIdx.x, G)) return;
+    const int32_t n_pos = min(a.sched.n_pos[blockIdx.x], kSchedMaxPos);
+    if (n_pos <= 0) return;
+    const bool consumer = wave < NW;
+    const bool active = consumer && G.r_lo + wave < G.r_hi;
+    const int64_t y = active ? G.r_lo + wave : G.r_hi - 1;
+    const int32_t t = a.rows.t_begin + (int32_t)(y - G.s_lo);
+    const int64_t qr = G.seq * a.rows.n_q + t;
+    const int32_t n_tok = a.vis.tokens(t);
+
+    // the plan into LDS (a position's ranks are 16 bytes)
+    {
+        const int32_t* pb = a.sched.blocks + (int64_t)blockIdx.x * a.sched.stride;
+        const u32x4* pr =
+            reinterpret_cast<const u32x4*>(a.sched.ranks + (int64_t)blockIdx.x * a.sched.stride * NW);
+        for (int i = threadIdx.x; i < n_pos; i += (NW + NP) * 64) {
+            s_blk[i] = pb[i];
+            reinterpret_cast<u32x4*>(s_rank)[i] = pr[i];
+        }
+    }
+    if (threadIdx.x < NS) {
+        s_ready[threadIdx.x] = -1;
+        s_done[threadIdx.x] = 0;
+    }
+    __syncthreads();
+
+    const int32_t bshift = a.block_shift;
+    const int32_t bmask = (1 << bshift) - 1;
+    const int32_t n_st = (int32_t)((((int64_t)n_pos << bshift) + RG::SK - 1) / RG::SK);
+    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.k) + G.seq * a.k_seq_len * (2 * D);
+    const int32_t kmax = (int32_t)(a.k_seq_len - 1);
+
+    if (!consumer) {
+#pragma unroll 1
+        for (int32_t x = wave - NW; x < n_st; x += NP) {
+            const int sl = x % NS;
+            const int32_t z0 = x * RG::SK;  // first slot of the stage
+            const int32_t pos0 = z0 >> bshift;
+            int32_t bk[4];  // blocks of the stage's positions (4 with 32-key blocks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bk[i] = pos0 + i < n_pos ? s_blk[pos0 + i] : -1;
+            const int32_t freed = NW * (x / NS);
+            spin_until([&] {
+                return __hip_atomic_load(&s_done[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= freed;
+            });
+            uint8_t* sp = ring + sl * RG::STAGE;
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) {
+                // piece p: slot z0 + p / 16 (row of the stage), physical chunk
+                // p % 16, logical chunk (p % 16) ^ (row % 16)
+                const int p = i * 64 + lane;
+                const int32_t z = z0 + (p >> 4);
+                const int32_t pi = (z >> bshift) - pos0;
+                const int32_t b = pi == 0 ? bk[0] : pi == 1 ? bk[1] : pi == 2 ? bk[2] : bk[3];
+                const int32_t key = b >= 0 ? min((b << bshift) + (z & bmask), kmax) : kmax;
+                const uint32_t chunk = (uint32_t)(((p & 15) ^ ((p >> 4) & 15)) * 16);
+                __builtin_amdgcn_global_load_lds(kseq + ((int64_t)key * (2 * D) + (int64_t)chunk),
+                                                 sp + i * 1024, 16, 0, 0);
+            }
+            wait_vmcnt<0>();
+            if (lane == 0) __hip_atomic_store(&s_ready[sl], x, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        return;
+    }
+
+    bf16x8 qa[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int h = mb * 32 + m;
+        if (h < a.heads) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(a.q + (qr * a.heads + h) * D + hf * (D / 2));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, p[ks]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        }
+    }
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int h = mb * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
+            wv[mb][j] = h < a.heads ? a.w[qr * a.heads + h] : 0.0f;
+        }
+    uint32_t roff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = m * (2 * D) + (((hf * 8 + ks) ^ (m & 15)) * 16);
+    float* orow = a.out + y * a.out_stride;
+
+#pragma unroll 1
+    for (int32_t st = 0; st < n_st; ++st) {
+        const int slot = st % NS;
+        // every stage is waited for, also one this row skips: a wave is then
+        // never more than NS - 1 stages ahead of the slowest, which is what
+        // makes the slot counts exact
+        spin_until([&] {
+            return __hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == st;
+        });
+        const uint8_t* sb = ring + slot * RG::STAGE;
+#pragma unroll
+        for (int j = 0; j < RG::SPS; ++j) {
+            const int32_t z = st * RG::SK + j * 32;  // slot of the sub-block's first key
+            const int32_t pos = z >> bshift;
+            if (pos >= n_pos) break;
+            const int32_t rank = s_rank[pos * NW + wave];
+            if (!active || rank < 0) continue;
+            const int32_t off = z & bmask;
+            const int32_t key0 = (s_blk[pos] << bshift) + off;
+            if (key0 >= n_tok) continue;
+            f32x16 acc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kb = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(sb + j * 32 * (2 * D) + roff[ks]));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+            }
+            float sc = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
+            sc = add_upper_half(sc);
+            if (hf == 0 && key0 + m < n_tok) orow[(rank << bshift) + off + m] = sc;
+        }
+        // done with the slot: its keys were read into registers above
+        if (lane == 0) __hip_atomic_fetch_add(&s_done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
 template <int MB, int NW>
 hipError_t launch_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     const int64_t R = a.rows.rows_per_seq;
@@ -1234,6 +1602,36 @@ hipError_t launch_d(const ScoreArgs& a, int64_t n_rows, bool fp8, bool blocks, h
 }
 
 }  // namespace
+
+int64_t refine_sched_groups(const RowMap& rows, int64_t n_rows) {
+    if (n_rows <= 0) return 0;
+    const int64_t R = rows.rows_per_seq;
+    const int64_t n_seq = (rows.y0 + n_rows - 1) / R - rows.y0 / R + 1;
+    return n_seq * ((std::min<int64_t>(n_rows, R) + kSchedRows - 1) / kSchedRows);
+}
+
+hipError_t launch_score_refine_sched(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
+    if (n_rows <= 0) return hipSuccess;
+    const RefineSched& P = a.sched;
+    if (P.stride < 4 || P.stride > kSchedMaxPos || P.stride % 4 || P.max_blocks < 1 ||
+        P.max_blocks > kSchedMaxBlocks || a.blk_stride < 1 || a.blk_stride > kMaxBlkEntries)
+        return hipErrorInvalidValue;
+    const int64_t R = a.rows.rows_per_seq;
+    const int32_t per_seq = (int32_t)((std::min<int64_t>(n_rows, R) + kSchedRows - 1) / kSchedRows);
+    const int64_t groups = refine_sched_groups(a.rows, n_rows);
+    const int32_t lds_blocks = (P.max_blocks + 63) / 64 * 64;
+    hipLaunchKernelGGL(refine_plan_kernel, dim3((unsigned)groups), dim3(64), plan_lds_bytes(lds_blocks, P.stride),
+                       stream, a, n_rows, per_seq, lds_blocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.heads > 32)
+        hipLaunchKernelGGL((refine_sched_kernel<2, 4, 3>), dim3((unsigned)groups), dim3((kSchedRows + 3) * 64), 0,
+                           stream, a, n_rows, per_seq);
+    else
+        hipLaunchKernelGGL((refine_sched_kernel<1, 4, 3>), dim3((unsigned)groups), dim3((kSchedRows + 3) * 64), 0,
+                           stream, a, n_rows, per_seq);
+    return hipGetLastError();
+}
 
 hipError_t launch_score_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0 || a.n_cols <= 0) return hipSuccess;

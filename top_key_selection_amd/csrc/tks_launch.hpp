@@ -26,6 +26,22 @@ struct FusedPool {
     int32_t r_cap;     // survivors per segment at most
 };
 
+// Refinement schedule (score.hip): for each group of kSchedRows consecutive
+// prefill rows of one sequence, the blocks any of them kept, in the order the
+// scheduled refinement copies them, with each row's position of the block in
+// its own list (-1: not kept).  Groups follow the rows of a chunk sequence by
+// sequence (as refine_sched_groups counts them).
+constexpr int kSchedRows = 8;
+constexpr int kSchedMaxPos = 1024;     // blocks of a group's union at most
+constexpr int kSchedMaxBlocks = 8192;  // visible blocks of a row at most
+struct RefineSched {
+    int32_t* n_pos;      // [groups]
+    int32_t* blocks;     // [groups, stride]
+    int16_t* ranks;      // [groups, stride, kSchedRows]
+    int32_t stride;      // positions per group in the layout: a multiple of 4, <= kSchedMaxPos
+    int32_t max_blocks;  // visible blocks of any row at most, <= kSchedMaxBlocks
+};
+
 // Scoring of one row chunk against a run of key slots (score.hip).
 //   contiguous mode: slot j is key col_key0 + j of the row's sequence;
 //   block mode:      slot j is key blk[row][j / B] * B + j % B.
@@ -52,6 +68,7 @@ struct ScoreArgs {
     int32_t stream_keys;    // each key row is read by one query row only (decode)
     FusedPool fuse;         // fused mode (fuse.cand != null): survivors instead of `out`
     int32_t* fuse_clear;    // fused mode: a counter the first workgroup sets to 0
+    RefineSched sched;      // scheduled refinement: the plan (written, then read)
 };
 
 // Exact top-k of row candidates (select.hip).  Candidates of a row are the
@@ -178,6 +195,12 @@ hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
 // by position through the shared-key ring; a.n_cols = keys of the run,
 // a.blk / a.blk_stride = block lists, a.out = [rows, blk_stride << shift])
 hipError_t launch_score_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream);
+// Groups of kSchedRows rows that a scheduled refinement of chunk rows
+// [0, n_rows) uses, and the launch itself: a plan kernel writes a.sched,
+// then the refinement scores each group's union of kept blocks in plan order
+// through the shared-key ring (bf16 keys, D = 128; a.out as above).
+int64_t refine_sched_groups(const RowMap& rows, int64_t n_rows);
+hipError_t launch_score_refine_sched(const ScoreArgs& a, int64_t n_rows, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int dim, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int64_t n_rows, hipStream_t stream);
 size_t attend_workspace(int64_t rows, int32_t heads, int32_t topk);
