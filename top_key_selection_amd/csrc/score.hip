@@ -1213,10 +1213,34 @@ __device__ __forceinline__ bool sched_group(const ScoreArgs& a, int64_t n_rows, 
 }
 
 // LDS of the plan kernel for `nb` (a multiple of 64) visible blocks and a
-// layout stride `P`: pattern words, block -> union index, union blocks,
-// union ranks, pattern counts, union patterns
+// layout stride `P` (a multiple of 4): pattern words, block -> union index,
+// union blocks, union ranks, pattern counts and offsets, union patterns,
+// pattern of each plan position, union indices by pattern
 __host__ __device__ constexpr size_t plan_lds_bytes(int32_t nb, int32_t P) {
-    return 3 * (size_t)nb + 21 * (size_t)P + 1024;
+    return 3 * (size_t)nb + 24 * (size_t)P + 2048;
+}
+
+// Largest value over the wave (gfx9 DPP: shifts within rows of 16 lanes,
+// then the row broadcasts; lane 63 ends with the maximum).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Lanes of the wave whose 8-bit value equals this lane's (one ballot per bit).
+__device__ __forceinline__ uint64_t match8(uint32_t v) {
+    uint64_t eq = ~0ull;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint64_t b = __ballot((v >> j) & 1u);
+        eq &= ((v >> j) & 1u) ? b : ~b;
+    }
+    return eq;
 }
 
 __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_rows, int32_t per_seq,
@@ -1246,7 +1270,10 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
     int32_t* ublk = reinterpret_cast<int32_t*>(plan_lds + 3 * (size_t)lds_blocks);  // [P]
     int16_t* urank = reinterpret_cast<int16_t*>(ublk + P.stride);        // [P, kSchedRows]
     int32_t* pcnt = reinterpret_cast<int32_t*>(urank + (size_t)P.stride * kSchedRows);  // [256]
-    uint8_t* upat = reinterpret_cast<uint8_t*>(pcnt + 256);              // [P]
+    int32_t* poff = pcnt + 256;                                          // [256]
+    uint8_t* upat = reinterpret_cast<uint8_t*>(poff + 256);              // [P]
+    uint8_t* seq = upat + P.stride;                                      // [P]
+    int16_t* bucket = reinterpret_cast<int16_t*>(seq + P.stride);        // [P]
 
     const int nw = (nbv + 3) >> 2;
     for (int i = lane; i < nw; i += 64) pw[i] = 0u;
@@ -1315,8 +1342,12 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
         for (int o = 32; o >= 1; o >>= 1) tot[j] += __shfl_xor(tot[j], o);
     __syncthreads();
 
-    // greedy over patterns: lane owns patterns 4 lane .. 4 lane + 3
-    int32_t T[4], Dn[4], C[4], CUR[4];
+    // phase 1, the greedy over patterns (registers only): lane owns
+    // patterns 4 lane .. 4 lane + 3; a pattern's key is its score shifted to
+    // be non-negative (|score| < 2^22: n <= 1024 blocks, row totals <= 512)
+    // with 255 - pattern below it, so the wave's largest key is the
+    // pattern to take (ties: the smaller one)
+    int32_t T[4], Dn[4], C[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int p = lane * 4 + k;
@@ -1325,55 +1356,79 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
         for (int j = 0; j < kSchedRows; ++j) T[k] += ((p >> j) & 1) * tot[j];
         Dn[k] = 0;
         C[k] = p == 0 ? 0 : pcnt[p];
-        CUR[k] = 0;
     }
-    int32_t* out_blk = P.blocks + (int64_t)blockIdx.x * P.stride;
-    int16_t* out_rank = P.ranks + (int64_t)blockIdx.x * P.stride * kSchedRows;
     for (int32_t st = 0; st < n_u; ++st) {
-        int32_t best = INT32_MIN, bp = 256;
+        uint32_t key = 0u;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int32_t sc = (st + 1) * T[k] - n_u * Dn[k];
-            if (C[k] > 0 && sc > best) {
-                best = sc;
-                bp = lane * 4 + k;
-            }
+            const uint32_t kk = ((uint32_t)(sc + (1 << 22)) << 8) | (uint32_t)(255 - (lane * 4 + k));
+            key = C[k] > 0 ? max(key, kk) : key;
         }
+        const int32_t ps = 255 - (int32_t)(wave_max_u32(key) & 255u);
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const int32_t ob = __shfl_xor(best, o);
-            const int32_t op = __shfl_xor(bp, o);
-            if (ob > best || (ob == best && op < bp)) {
-                best = ob;
-                bp = op;
-            }
+        for (int k = 0; k < 4; ++k) {
+            Dn[k] += __builtin_popcount((uint32_t)((lane * 4 + k) & ps));
+            C[k] -= (lane * 4 + k) == ps ? 1 : 0;
         }
-        const int32_t ps = __builtin_amdgcn_readfirstlane(bp);  // has blocks left
-        const int owner = ps >> 2;
-        const int ks = ps & 3;
+        if (lane == 0) seq[st] = (uint8_t)ps;
+    }
+    // each pattern's union entries in ascending order: offsets, then a rank
+    // among equal patterns for every entry (64 entries at a time)
+    {
+        int32_t c4[4], s4 = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) Dn[k] += __builtin_popcount((uint32_t)((lane * 4 + k) & ps));
-        const int32_t my_cur = ks == 0 ? CUR[0] : ks == 1 ? CUR[1] : ks == 2 ? CUR[2] : CUR[3];
-        // the pattern's next block in ascending order, 64 union entries at a time
+        for (int k = 0; k < 4; ++k) {
+            c4[k] = pcnt[lane * 4 + k];
+            s4 += c4[k];
+        }
+        int32_t inc4 = s4;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t t = __shfl_up(inc4, o);
+            if (lane >= o) inc4 += t;
+        }
+        int32_t run = inc4 - s4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            poff[lane * 4 + k] = run;
+            run += c4[k];
+        }
+    }
+    __syncthreads();
+    for (int i = lane; i < 256; i += 64) pcnt[i] = 0;  // running counts per pattern
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int32_t c = 0; c < n_u; c += 64) {
+        const int32_t u = c + lane;
+        const uint32_t pu = u < n_u ? (uint32_t)upat[u] : 0u;  // 0: no entry
+        const uint64_t eq = match8(pu) & __ballot(u < n_u);
+        if (u < n_u) bucket[poff[pu] + pcnt[pu] + __popcll(eq & below)] = (int16_t)u;
+        __syncthreads();
+        if (u < n_u && (eq & below) == 0ull) pcnt[pu] += __popcll(eq);  // the group's first lane
+        __syncthreads();
+    }
+    for (int i = lane; i < 256; i += 64) pcnt[i] = 0;
+    __syncthreads();
+    // phase 2: position st takes the next block of its pattern
+    int32_t* out_blk = P.blocks + (int64_t)blockIdx.x * P.stride;
+    int16_t* out_rank = P.ranks + (int64_t)blockIdx.x * P.stride * kSchedRows;
+    for (int32_t c = 0; c < n_u; c += 64) {
+        const int32_t st = c + lane;
+        const uint32_t ps = st < n_u ? (uint32_t)seq[st] : 0u;
+        const uint64_t eq = match8(ps) & __ballot(st < n_u);
         int32_t uu = 0;
-        for (int32_t c = __shfl(my_cur, owner); c < n_u; c += 64) {
-            const int32_t idx = c + lane;
-            const uint64_t hit = __ballot(idx < n_u && upat[idx] == (uint32_t)ps);
-            if (hit != 0ull) {
-                uu = c + __builtin_ctzll(hit);
-                break;
-            }
+        if (st < n_u) {
+            uu = bucket[poff[ps] + pcnt[ps] + __popcll(eq & below)];
+            out_blk[st] = ublk[uu];
+            const uint64_t rk = *reinterpret_cast<const uint64_t*>(urank + uu * kSchedRows);
+            const uint64_t rk2 = *reinterpret_cast<const uint64_t*>(urank + uu * kSchedRows + 4);
+            reinterpret_cast<uint64_t*>(out_rank + (int64_t)st * kSchedRows)[0] = rk;
+            reinterpret_cast<uint64_t*>(out_rank + (int64_t)st * kSchedRows)[1] = rk2;
         }
-        if (lane == owner) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (k == ks) {
-                    CUR[k] = uu + 1;
-                    C[k] -= 1;
-                }
-        }
-        if (lane == 0) out_blk[st] = ublk[uu];
-        if (lane < kSchedRows) out_rank[(int64_t)st * kSchedRows + lane] = urank[uu * kSchedRows + lane];
+        __syncthreads();
+        if (st < n_u && (eq & below) == 0ull) pcnt[ps] += __popcll(eq);
+        __syncthreads();
     }
     if (lane == 0) P.n_pos[blockIdx.x] = n_u;
 }
