@@ -311,6 +311,34 @@ def test_scheduled_refine_block_sizes_exact(block, m_scored, n_k, q_chunk):
                       "scheduled refine B=%d" % block)
 
 
+def test_refine_plans_made_chunk_by_chunk_exact():
+    """Refinement plans too large to make for every group at once (here
+    4096 groups x 1024 positions) are made chunk by chunk; with 1000-row
+    chunks, groups of 8 queries straddle chunk boundaries and each chunk
+    refines only its own rows of them.  Sampled rows at chunk and group
+    boundaries must equal the oracle's blocks and tokens."""
+    say("refine, plans per chunk: 32768 queries, 33000 keys, B=32, m_total 128, q_chunk 1000")
+    n_q, n_k, heads, block, m_scored, topk = 32768, 33000, 8, 32, 126, 512
+    flags = FORCE_FIRST | FORCE_LOCAL
+    sh, x = int_case(93, batch=1, n_q=n_q, n_k=n_k, heads=heads, dim=128, q_pos0=n_k - n_q,
+                     lo=-2, hi=2)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 7, 8, 999, 1000, 1001, 1007, 1008, 15999, 16000, 16001,
+                                      31999, 32000, 32767], rng.choice(n_q, 34, replace=False)]))
+    qr = x["q"].reshape(n_q, heads, 128)[rows]
+    wr = x["w"].reshape(n_q, heads)[rows]
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, block, m_scored, flags, topk, rows)
+    S = tks.Shape(**sh)
+    q, w, k, ks = gpu_inputs(x)
+    pooled = tks.hisa_pool_keys(S, k, ks, block)
+    blk, _ = tks.hisa_block_select(S, q, w, pooled, block, m_scored, flags, with_vals=False)
+    idx, vals = tks.hisa_refine_topk(S, q, w, k, ks, block, blk, topk, 1000)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(n_q, -1)[rows], blk_o)
+    assert_topk_exact(host(idx).reshape(n_q, -1)[rows], host(vals).reshape(n_q, -1)[rows], idx_o,
+                      val_o, "plans per chunk")
+
+
 def test_refine_lists_too_long_for_a_plan_take_the_segment_ring_exact():
     """A group's union of kept blocks can exceed what one plan holds (here
     8 rows x 150 entries over 1250 blocks of 32 keys): such shapes refine

@@ -748,6 +748,10 @@ int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, con
 
 namespace {
 
+// the refinement plans of every group are made in one launch when their
+// arrays take at most this many bytes (else chunk by chunk)
+constexpr int64_t kPlanAllBytes = (int64_t)64 << 20;
+
 struct RefinePlan {
     int64_t rows;
     int32_t slots;
@@ -755,9 +759,10 @@ struct RefinePlan {
     int64_t stride;
     bool shared;        // prefill rows, bf16 keys, dim 128: the shared-key ring
     bool sched;         // ... with a plan per group of rows (bounded sizes)
+    bool plan_all;      // one plan launch for every group of the call
     int32_t sched_stride;
     int32_t sched_blocks;
-    int64_t groups;     // plan groups of a chunk at most
+    int64_t groups;     // plan slots: every group, or a chunk's groups at most
     size_t off_n, off_blk, off_rank;  // plan arrays in the workspace
     size_t bytes;
 };
@@ -779,9 +784,14 @@ RefinePlan plan_refine(const tks_shape* s, int32_t block, int32_t m_total, int32
     if (p.sched) {
         p.sched_stride = (int32_t)round_up(pu, 4);
         p.sched_blocks = (int32_t)nb_all;
-        const int64_t per_seq = (std::min<int64_t>(p.chunk, s->n_q) + tks::kSchedRows - 1) / tks::kSchedRows;
-        const int64_t n_seq = std::min<int64_t>(s->batch, (p.chunk + s->n_q - 1) / s->n_q + 1);
-        p.groups = n_seq * per_seq;
+        // groups of kSchedRows queries of a sequence; a chunk of c rows
+        // touches at most c / kSchedRows + 1 of them per sequence it starts
+        // or ends in, and enters at most c / n_q + 2 sequences
+        const int64_t all = (int64_t)s->batch * ((s->n_q + tks::kSchedRows - 1) / tks::kSchedRows);
+        const int64_t per_chunk = std::min<int64_t>(
+            all, (p.chunk + tks::kSchedRows - 1) / tks::kSchedRows + (p.chunk + s->n_q - 1) / s->n_q + 3);
+        p.plan_all = all * p.sched_stride * (4 + 2 * tks::kSchedRows) <= kPlanAllBytes;
+        p.groups = p.plan_all ? all : per_chunk;
         p.off_n = p.bytes;
         p.off_blk = p.off_n + round_up(p.groups * 4, 256);
         p.off_rank = p.off_blk + round_up(p.groups * p.sched_stride * 4, 256);
@@ -856,8 +866,19 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
                 a.sched.ranks = reinterpret_cast<int16_t*>(base + p.off_rank);
                 a.sched.stride = p.sched_stride;
                 a.sched.max_blocks = p.sched_blocks;
-                e = tks::refine_sched_groups(rm, n) > p.groups ? hipErrorInvalidValue
-                                                                : tks::launch_score_refine_sched(a, n, stream);
+                int64_t g_lo, g_hi;
+                tks::refine_sched_groups(rm, n, g_lo, g_hi);
+                // the plans: every group with the first chunk, or this chunk's
+                e = hipSuccess;
+                if (p.plan_all) {
+                    a.sched.group0 = 0;
+                    if (g0 == 0) e = tks::launch_refine_plan(a, 0, p.groups, stream);
+                } else {
+                    a.sched.group0 = g_lo;
+                    e = g_hi - g_lo > p.groups ? hipErrorInvalidValue
+                                               : tks::launch_refine_plan(a, g_lo, g_hi, stream);
+                }
+                if (e == hipSuccess) e = tks::launch_score_refine_sched(a, n, stream);
             } else if (p.shared) {
                 // keys of the run: up to the last visible key of the chunk
                 a.n_cols = max_visible(s, g0, g0 + n);

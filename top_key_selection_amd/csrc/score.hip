@@ -1194,22 +1194,19 @@ hipError_t launch_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t 
 // ties go to the smaller pattern, and a pattern's blocks go in ascending
 // order, so the plan is a function of the block lists alone.
 
+// Group g of a call: queries [t0, t0 + nr) of sequence seq.
 struct SchedGroup {
-    int64_t s_lo;  // chunk row of the sequence's first row (may be negative)
-    int64_t r_lo, r_hi;
     int64_t seq;
+    int32_t t0, nr;
 };
 
-__device__ __forceinline__ bool sched_group(const ScoreArgs& a, int64_t n_rows, int32_t per_seq,
-                                            int64_t g, SchedGroup& G) {
-    const int64_t R = a.rows.rows_per_seq;
-    G.seq = a.rows.y0 / R + g / per_seq;
-    G.s_lo = G.seq * R - a.rows.y0;
-    const int64_t lo = G.s_lo > 0 ? G.s_lo : 0;
-    const int64_t hi = G.s_lo + R < n_rows ? G.s_lo + R : n_rows;
-    G.r_lo = lo + (g % per_seq) * kSchedRows;
-    G.r_hi = G.r_lo + kSchedRows < hi ? G.r_lo + kSchedRows : hi;
-    return G.r_lo < hi;
+__device__ __forceinline__ SchedGroup sched_group(int32_t n_q, int64_t g) {
+    const int64_t per = (n_q + kSchedRows - 1) / kSchedRows;
+    SchedGroup G;
+    G.seq = g / per;
+    G.t0 = (int32_t)(g % per) * kSchedRows;
+    G.nr = min(kSchedRows, n_q - G.t0);
+    return G;
 }
 
 // LDS of the plan kernel for `nb` (a multiple of 64) visible blocks and a
@@ -1243,17 +1240,15 @@ __device__ __forceinline__ uint64_t match8(uint32_t v) {
     return eq;
 }
 
-__global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_rows, int32_t per_seq,
-                                                         int32_t lds_blocks) {
+__global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t g_lo, int32_t lds_blocks) {
     extern __shared__ __align__(16) uint8_t plan_lds[];
     const int lane = threadIdx.x;
     const RefineSched P = a.sched;
-    SchedGroup G;
-    if (!sched_group(a, n_rows, per_seq, blockIdx.x, G)) {
-        if (lane == 0) P.n_pos[blockIdx.x] = 0;
-        return;
-    }
-    const int nr = (int)(G.r_hi - G.r_lo);
+    const int64_t gid = g_lo + blockIdx.x;
+    const int64_t slot = gid - P.group0;
+    const SchedGroup G = sched_group(a.rows.n_q, gid);
+    const int nr = G.nr;
+    const int64_t row0 = G.seq * a.rows.n_q + G.t0;  // global row of the group's first query
     const int32_t bshift = a.block_shift;
     const int32_t m_total = a.blk_stride;
     // blocks with a visible key, per row and for the group
@@ -1261,7 +1256,7 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
     int32_t nbv = 0;
 #pragma unroll
     for (int j = 0; j < kSchedRows; ++j) {
-        const int32_t n_tok = j < nr ? a.vis.tokens(a.rows.t_begin + (int32_t)(G.r_lo + j - G.s_lo)) : 0;
+        const int32_t n_tok = j < nr ? a.vis.tokens(G.t0 + j) : 0;
         nbv_row[j] = n_tok > 0 ? min(((n_tok - 1) >> bshift) + 1, lds_blocks) : 0;
         nbv = max(nbv, nbv_row[j]);
     }
@@ -1281,7 +1276,7 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
     __syncthreads();
     // patterns: bit j of block b's byte = row j kept b
     for (int j = 0; j < nr; ++j) {
-        const int32_t* lst = a.blk + (a.rows.y0 + G.r_lo + j) * (int64_t)m_total;
+        const int32_t* lst = a.blk + (row0 + j) * (int64_t)m_total;
         for (int i = lane; i < m_total; i += 64) {
             const int32_t e = lst[i];
             if (e >= 0 && e < nbv_row[j]) atomicOr(&pw[e >> 2], 1u << (8 * (e & 3) + j));
@@ -1330,7 +1325,7 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
         for (int j = 0; j < kSchedRows; ++j) tot[j] += (pat >> j) & 1u;
     }
     for (int j = 0; j < nr; ++j) {
-        const int32_t* lst = a.blk + (a.rows.y0 + G.r_lo + j) * (int64_t)m_total;
+        const int32_t* lst = a.blk + (row0 + j) * (int64_t)m_total;
         for (int i = lane; i < m_total; i += 64) {
             const int32_t e = lst[i];
             if (e >= 0 && e < nbv_row[j]) urank[umap[e] * kSchedRows + j] = (int16_t)i;
@@ -1411,8 +1406,8 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
     for (int i = lane; i < 256; i += 64) pcnt[i] = 0;
     __syncthreads();
     // phase 2: position st takes the next block of its pattern
-    int32_t* out_blk = P.blocks + (int64_t)blockIdx.x * P.stride;
-    int16_t* out_rank = P.ranks + (int64_t)blockIdx.x * P.stride * kSchedRows;
+    int32_t* out_blk = P.blocks + slot * P.stride;
+    int16_t* out_rank = P.ranks + slot * P.stride * kSchedRows;
     for (int32_t c = 0; c < n_u; c += 64) {
         const int32_t st = c + lane;
         const uint32_t ps = st < n_u ? (uint32_t)seq[st] : 0u;
@@ -1430,7 +1425,7 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
         if (st < n_u && (eq & below) == 0ull) pcnt[ps] += __popcll(eq);
         __syncthreads();
     }
-    if (lane == 0) P.n_pos[blockIdx.x] = n_u;
+    if (lane == 0) P.n_pos[slot] = n_u;
 }
 
 // One workgroup per group: kSchedRows consumer waves (one row each) and NP
@@ -1441,7 +1436,7 @@ __global__ __launch_bounds__(64) void refine_plan_kernel(ScoreArgs a, int64_t n_
 // before issuing its copies; consumers issue no copies at all.
 template <int MB, int NS, int NP>
 __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(ScoreArgs a, int64_t n_rows,
-                                                                            int32_t per_seq) {
+                                                                            int64_t g_lo) {
     using RG = SharedRing;
     constexpr int NW = kSchedRows;
     constexpr int D = RG::D;
@@ -1458,22 +1453,25 @@ __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(Sc
     const int m = lane & 31;
     const int hf = lane >> 5;
 
-    SchedGroup G;
-    if (!sched_group(a, n_rows, per_seq, blockIdx.x, G)) return;
-    const int32_t n_pos = min(a.sched.n_pos[blockIdx.x], kSchedMaxPos);
+    const int64_t gid = g_lo + blockIdx.x;
+    const int64_t slot_g = gid - a.sched.group0;
+    const SchedGroup G = sched_group(a.rows.n_q, gid);
+    const int32_t n_pos = min(a.sched.n_pos[slot_g], kSchedMaxPos);
     if (n_pos <= 0) return;
     const bool consumer = wave < NW;
-    const bool active = consumer && G.r_lo + wave < G.r_hi;
-    const int64_t y = active ? G.r_lo + wave : G.r_hi - 1;
-    const int32_t t = a.rows.t_begin + (int32_t)(y - G.s_lo);
+    // this wave's query and its chunk row (rows of the group outside the
+    // chunk are left out)
+    const int32_t t = G.t0 + min(wave, G.nr - 1);
     const int64_t qr = G.seq * a.rows.n_q + t;
+    const int64_t yc = qr - a.rows.y0;
+    const bool active = consumer && wave < G.nr && yc >= 0 && yc < n_rows;
+    const int64_t y = active ? yc : 0;
     const int32_t n_tok = a.vis.tokens(t);
 
     // the plan into LDS (a position's ranks are 16 bytes)
     {
-        const int32_t* pb = a.sched.blocks + (int64_t)blockIdx.x * a.sched.stride;
-        const u32x4* pr =
-            reinterpret_cast<const u32x4*>(a.sched.ranks + (int64_t)blockIdx.x * a.sched.stride * NW);
+        const int32_t* pb = a.sched.blocks + slot_g * a.sched.stride;
+        const u32x4* pr = reinterpret_cast<const u32x4*>(a.sched.ranks + slot_g * a.sched.stride * NW);
         for (int i = threadIdx.x; i < n_pos; i += (NW + NP) * 64) {
             s_blk[i] = pb[i];
             reinterpret_cast<u32x4*>(s_rank)[i] = pr[i];
@@ -1658,33 +1656,42 @@ hipError_t launch_d(const ScoreArgs& a, int64_t n_rows, bool fp8, bool blocks, h
 
 }  // namespace
 
-int64_t refine_sched_groups(const RowMap& rows, int64_t n_rows) {
-    if (n_rows <= 0) return 0;
-    const int64_t R = rows.rows_per_seq;
-    const int64_t n_seq = (rows.y0 + n_rows - 1) / R - rows.y0 / R + 1;
-    return n_seq * ((std::min<int64_t>(n_rows, R) + kSchedRows - 1) / kSchedRows);
+void refine_sched_groups(const RowMap& rows, int64_t n_rows, int64_t& g_lo, int64_t& g_hi) {
+    g_lo = g_hi = 0;
+    if (n_rows <= 0 || rows.n_q <= 0) return;
+    const int64_t per = (rows.n_q + kSchedRows - 1) / kSchedRows;
+    auto group_of = [&](int64_t global_row) {
+        return (global_row / rows.n_q) * per + (global_row % rows.n_q) / kSchedRows;
+    };
+    g_lo = group_of(rows.y0);
+    g_hi = group_of(rows.y0 + n_rows - 1) + 1;
+}
+
+hipError_t launch_refine_plan(const ScoreArgs& a, int64_t g_lo, int64_t g_hi, hipStream_t stream) {
+    const RefineSched& P = a.sched;
+    if (g_hi <= g_lo) return hipSuccess;
+    if (P.stride < 4 || P.stride > kSchedMaxPos || P.stride % 4 || P.max_blocks < 1 ||
+        P.max_blocks > kSchedMaxBlocks || a.blk_stride < 1 || a.blk_stride > kMaxBlkEntries ||
+        g_lo < P.group0 || a.rows.rows_per_seq != a.rows.n_q || a.rows.t_begin != 0 || g_hi - g_lo > INT32_MAX)
+        return hipErrorInvalidValue;
+    const int32_t lds_blocks = (P.max_blocks + 63) / 64 * 64;
+    hipLaunchKernelGGL(refine_plan_kernel, dim3((unsigned)(g_hi - g_lo)), dim3(64),
+                       plan_lds_bytes(lds_blocks, P.stride), stream, a, g_lo, lds_blocks);
+    return hipGetLastError();
 }
 
 hipError_t launch_score_refine_sched(const ScoreArgs& a, int64_t n_rows, hipStream_t stream) {
     if (n_rows <= 0) return hipSuccess;
-    const RefineSched& P = a.sched;
-    if (P.stride < 4 || P.stride > kSchedMaxPos || P.stride % 4 || P.max_blocks < 1 ||
-        P.max_blocks > kSchedMaxBlocks || a.blk_stride < 1 || a.blk_stride > kMaxBlkEntries)
-        return hipErrorInvalidValue;
-    const int64_t R = a.rows.rows_per_seq;
-    const int32_t per_seq = (int32_t)((std::min<int64_t>(n_rows, R) + kSchedRows - 1) / kSchedRows);
-    const int64_t groups = refine_sched_groups(a.rows, n_rows);
-    const int32_t lds_blocks = (P.max_blocks + 63) / 64 * 64;
-    hipLaunchKernelGGL(refine_plan_kernel, dim3((unsigned)groups), dim3(64), plan_lds_bytes(lds_blocks, P.stride),
-                       stream, a, n_rows, per_seq, lds_blocks);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (a.rows.rows_per_seq != a.rows.n_q || a.rows.t_begin != 0) return hipErrorInvalidValue;
+    int64_t g_lo, g_hi;
+    refine_sched_groups(a.rows, n_rows, g_lo, g_hi);
+    if (g_lo < a.sched.group0 || g_hi - g_lo > INT32_MAX) return hipErrorInvalidValue;
     if (a.heads > 32)
-        hipLaunchKernelGGL((refine_sched_kernel<2, 4, 3>), dim3((unsigned)groups), dim3((kSchedRows + 3) * 64), 0,
-                           stream, a, n_rows, per_seq);
+        hipLaunchKernelGGL((refine_sched_kernel<2, 4, 3>), dim3((unsigned)(g_hi - g_lo)),
+                           dim3((kSchedRows + 3) * 64), 0, stream, a, n_rows, g_lo);
     else
-        hipLaunchKernelGGL((refine_sched_kernel<1, 4, 3>), dim3((unsigned)groups), dim3((kSchedRows + 3) * 64), 0,
-                           stream, a, n_rows, per_seq);
+        hipLaunchKernelGGL((refine_sched_kernel<1, 4, 3>), dim3((unsigned)(g_hi - g_lo)),
+                           dim3((kSchedRows + 3) * 64), 0, stream, a, n_rows, g_lo);
     return hipGetLastError();
 }
 

@@ -27,19 +27,21 @@ struct FusedPool {
 };
 
 // Refinement schedule (score.hip): for each group of kSchedRows consecutive
-// prefill rows of one sequence, the blocks any of them kept, in the order the
-// scheduled refinement copies them, with each row's position of the block in
-// its own list (-1: not kept).  Groups follow the rows of a chunk sequence by
-// sequence (as refine_sched_groups counts them).
+// queries of one sequence (group g of the call: sequence g / G, queries
+// kSchedRows * (g % G) on, G = ceil(n_q / kSchedRows)), the blocks any of
+// them kept, in the order the scheduled refinement copies them, with each
+// row's position of the block in its own list (-1: not kept).  Plan slot
+// g - group0 holds group g.
 constexpr int kSchedRows = 8;
 constexpr int kSchedMaxPos = 1024;     // blocks of a group's union at most
 constexpr int kSchedMaxBlocks = 8192;  // visible blocks of a row at most
 struct RefineSched {
-    int32_t* n_pos;      // [groups]
-    int32_t* blocks;     // [groups, stride]
-    int16_t* ranks;      // [groups, stride, kSchedRows]
+    int32_t* n_pos;      // [slots]
+    int32_t* blocks;     // [slots, stride]
+    int16_t* ranks;      // [slots, stride, kSchedRows]
     int32_t stride;      // positions per group in the layout: a multiple of 4, <= kSchedMaxPos
     int32_t max_blocks;  // visible blocks of any row at most, <= kSchedMaxBlocks
+    int64_t group0;      // group of plan slot 0
 };
 
 // Scoring of one row chunk against a run of key slots (score.hip).
@@ -195,11 +197,13 @@ hipError_t launch_pool(const PoolArgs& a, bool fp8, hipStream_t stream);
 // by position through the shared-key ring; a.n_cols = keys of the run,
 // a.blk / a.blk_stride = block lists, a.out = [rows, blk_stride << shift])
 hipError_t launch_score_refine_shared(const ScoreArgs& a, int64_t n_rows, hipStream_t stream);
-// Groups of kSchedRows rows that a scheduled refinement of chunk rows
-// [0, n_rows) uses, and the launch itself: a plan kernel writes a.sched,
-// then the refinement scores each group's union of kept blocks in plan order
-// through the shared-key ring (bf16 keys, D = 128; a.out as above).
-int64_t refine_sched_groups(const RowMap& rows, int64_t n_rows);
+// Scheduled refinement (bf16 keys, D = 128): the groups [g_lo, g_hi) that
+// chunk rows [0, n_rows) touch; the plan of groups [g_lo, g_hi) (a.sched
+// written, a.rows only for n_q); and the refinement of the chunk rows, each
+// group's union of kept blocks scored in plan order through the shared-key
+// ring (a.out as above; rows of a group outside the chunk are left out).
+void refine_sched_groups(const RowMap& rows, int64_t n_rows, int64_t& g_lo, int64_t& g_hi);
+hipError_t launch_refine_plan(const ScoreArgs& a, int64_t g_lo, int64_t g_hi, hipStream_t stream);
 hipError_t launch_score_refine_sched(const ScoreArgs& a, int64_t n_rows, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int dim, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int64_t n_rows, hipStream_t stream);
