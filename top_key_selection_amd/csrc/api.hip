@@ -194,10 +194,13 @@ FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_
             qc = std::max<int64_t>(1, kScoreBudget / (kt * 4));
         }
         // one tile would hold every row's scores of every visible key:
-        // split the rows into four chunks (a single row: two key tiles)
+        // split the rows into two chunks, so at most half of them are held
+        // at once (a single row: two key tiles).  (Four chunks measured 7 %
+        // slower at 8K prefill: the early chunks of the causal triangle are
+        // too small to fill the GPU.)
         if (qc >= p.rows && kt >= maxvis) {
             if (p.rows > 1)
-                qc = (p.rows + 3) / 4;
+                qc = (p.rows + 1) / 2;
             else if (k_tile <= 0 && maxvis > 32)
                 kt = round_up((maxvis + 1) / 2, 32);
         }
