@@ -951,15 +951,18 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
 // the number of the stage it has.  Waits are sleep loops: a consumer waits
 // only for a producer, which waits only for consumers finishing an earlier
 // stage, so every loop ends; the bound keeps a kernel from hanging forever
-// should that reasoning fail.
+// should that reasoning fail, and then the failure shows in the output: the
+// wave raises the workgroup's flag and consumers store NaN scores from then
+// on, which no selection passes as a correct result.
 constexpr int32_t kRingSpinMax = 1 << 22;
 
 template <typename F>
-__device__ __forceinline__ void spin_until(F&& ok) {
+__device__ __forceinline__ void spin_until(F&& ok, int32_t* fail) {
     for (int32_t spin = 0; spin < kRingSpinMax; ++spin) {
         if (ok()) return;
         __builtin_amdgcn_s_sleep(1);
     }
+    __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // NW rows per workgroup, NS ring stages of 128 keys (32 KiB), NP producers.
@@ -977,6 +980,7 @@ __global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs
     __shared__ __align__(16) uint8_t ring[NS * RG::STAGE];
     __shared__ int32_t s_ready[NS];                 // stage held by each slot
     __shared__ int32_t s_done[NS];                  // consumers done, all stages of the slot
+    __shared__ int32_t s_fail;                      // a bounded wait ran out
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m = lane & 31;
@@ -1052,6 +1056,7 @@ __global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs
     if (threadIdx.x < NS) {
         s_ready[threadIdx.x] = threadIdx.x < n_st ? (int32_t)threadIdx.x : -1;
         s_done[threadIdx.x] = 0;
+        if (threadIdx.x == 0) s_fail = 0;
     }
     wait_vmcnt<0>();
     __syncthreads();  // the first stages and the slot states
@@ -1061,9 +1066,11 @@ __global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs
         for (int32_t x = NS + (wave - NW); x < n_st; x += NP) {
             const int sl = x % NS;
             const int32_t freed = NW * (x / NS);
-            spin_until([&] {
-                return __hip_atomic_load(&s_done[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= freed;
-            });
+            spin_until(
+                [&] {
+                    return __hip_atomic_load(&s_done[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= freed;
+                },
+                &s_fail);
             uint8_t* sp = ring + sl * RG::STAGE;
 #pragma unroll
             for (int i = 0; i < PIECES; ++i) copy_piece(sp, slot_begin + x * RG::SK, i * 64 + lane);
@@ -1117,9 +1124,11 @@ __global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs
         // every stage is waited for, also one this row skips: a wave is then
         // never more than NS - 1 stages ahead of the slowest, which is what
         // makes the slot counts exact
-        spin_until([&] {
-            return __hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == st;
-        });
+        spin_until(
+            [&] {
+                return __hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == st;
+            },
+            &s_fail);
         const uint8_t* sb = ring + slot * RG::STAGE;
 #pragma unroll
         for (int j = 0; j < RG::SPS; ++j) {
@@ -1149,6 +1158,7 @@ __global__ __launch_bounds__((NW + NP) * 64) void refine_shared_kernel(ScoreArgs
                 for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
             sc = add_upper_half(sc);
             const int32_t key = key0 + m;
+            if (__hip_atomic_load(&s_fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) sc = __builtin_nanf("");
             if (hf == 0 && key < n_tok) orow[ptr * (bmask + 1) + (key & bmask)] = sc;
         }
         // done with the slot: its keys were read into registers above
@@ -1448,6 +1458,7 @@ __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(Sc
     __shared__ __align__(16) int16_t s_rank[kSchedMaxPos * NW];
     __shared__ int32_t s_ready[NS];  // stage held by each slot
     __shared__ int32_t s_done[NS];   // consumers done, all stages of the slot
+    __shared__ int32_t s_fail;       // a bounded wait ran out
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m = lane & 31;
@@ -1480,6 +1491,7 @@ __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(Sc
     if (threadIdx.x < NS) {
         s_ready[threadIdx.x] = -1;
         s_done[threadIdx.x] = 0;
+        if (threadIdx.x == 0) s_fail = 0;
     }
     __syncthreads();
 
@@ -1499,9 +1511,11 @@ __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(Sc
 #pragma unroll
             for (int i = 0; i < 4; ++i) bk[i] = pos0 + i < n_pos ? s_blk[pos0 + i] : -1;
             const int32_t freed = NW * (x / NS);
-            spin_until([&] {
-                return __hip_atomic_load(&s_done[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= freed;
-            });
+            spin_until(
+                [&] {
+                    return __hip_atomic_load(&s_done[sl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= freed;
+                },
+                &s_fail);
             uint8_t* sp = ring + sl * RG::STAGE;
 #pragma unroll
             for (int i = 0; i < PIECES; ++i) {
@@ -1554,9 +1568,11 @@ __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(Sc
         // every stage is waited for, also one this row skips: a wave is then
         // never more than NS - 1 stages ahead of the slowest, which is what
         // makes the slot counts exact
-        spin_until([&] {
-            return __hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == st;
-        });
+        spin_until(
+            [&] {
+                return __hip_atomic_load(&s_ready[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == st;
+            },
+            &s_fail);
         const uint8_t* sb = ring + slot * RG::STAGE;
 #pragma unroll
         for (int j = 0; j < RG::SPS; ++j) {
@@ -1587,6 +1603,7 @@ __global__ __launch_bounds__((kSchedRows + NP) * 64) void refine_sched_kernel(Sc
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sc = fmaf(wv[mb][i], relu_bits(acc[mb][i]), sc);
             sc = add_upper_half(sc);
+            if (__hip_atomic_load(&s_fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) sc = __builtin_nanf("");
             if (hf == 0 && key0 + m < n_tok) orow[(rank << bshift) + off + m] = sc;
         }
         // done with the slot: its keys were read into registers above
