@@ -298,9 +298,12 @@ int tks_sparse_attention(const void* q, const void* k, const void* v, int32_t ba
  * earlier records.  tks_profile_read() waits for the recorded events and
  * returns the summed duration and launch count of one kernel role:
  *   "score_flat"    -- token scoring of tks_topk_flat / tks_indexer_scores
+ *                      (fused form: scoring with the segment filter)
  *   "score_pooled"  -- pooled-block scoring of tks_hisa_block_select
- *   "score_refine"  -- gathered-block scoring of tks_hisa_refine_topk
- *   "select_flat"   -- top-k selection of tks_topk_flat
+ *   "score_refine"  -- scoring of the kept blocks in tks_hisa_refine_topk
+ *                      (prefill: with the refinement plans)
+ *   "select_flat"   -- top-k selection of tks_topk_flat (fused form: the
+ *                      finish and the repair launch)
  *   "select_pooled" -- block selection of tks_hisa_block_select
  *   "select_refine" -- top-k selection of tks_hisa_refine_topk
  *   "select_scores" -- tks_topk_scores

@@ -927,16 +927,14 @@ __global__ __launch_bounds__(NW * 64) void score_shared_kernel(ScoreArgs a, int6
 
 // ------------------------------------------------------------------------
 // HISA refinement for prefill (HISA abstract: the token indexer again, only
-// inside each query's kept blocks).  Neighbouring queries keep nearly
-// disjoint block sets (sixteen neighbours together keep nearly every visible
-// block), so no key is shared by many queries' block lists; the keys are
-// shared by position instead.  The workgroup is the shared-key one: NW
-// consecutive query rows, one per wave, and the same LDS ring streaming a
-// run of keys for all of them.  A wave runs the MFMAs and head reduction of
-// a 32-key sub-block only when its row kept the sub-block's block, found by
-// walking the row's ascending block list alongside the keys, and writes the
-// scores to the row's slots e * B + (key mod B) for list entry e.  The
-// arithmetic is the flat kernel's, so the scores are the same fp32 values.
+// inside each query's kept blocks).  The keys are shared by position: the
+// workgroup is the shared-key one (consecutive queries of one sequence, one
+// per wave, a ring of key stages), and a wave runs the MFMAs and head
+// reduction of a 32-key sub-block only when its row kept the sub-block's
+// block, writing the scores to the row's slots e * B + (key mod B) for list
+// entry e.  The arithmetic is the flat kernel's, so the scores are the same
+// fp32 values.
+//
 // Refinement over a shared key ring with producer and consumer waves.
 // NW consumer waves (one query row each) walk the ring at their own pace:
 // a wave skips the sub-blocks its row did not keep and may run up to NS - 1
