@@ -417,6 +417,29 @@ def test_fp8_decode_stream_path_exact(dim, heads):
                       "fp8 decode hisa")
 
 
+@pytest.mark.parametrize("fp8,batch,n_q,n_k", [(True, 2, 64, 1100), (False, 4, 1, 3001)])
+def test_hisa_generic_block_paths_exact(fp8, batch, n_q, n_k):
+    """HISA through the per-row block-mode scoring: prefill with fp8 keys
+    (pooled blocks of dequantised keys) and decode with bf16 keys, 64 heads,
+    ragged caches.  Blocks and tokens must equal the oracle's."""
+    say("HISA generic block paths fp8=%d batch=%d n_q=%d n_k=%d" % (fp8, batch, n_q, n_k))
+    block, m_scored, topk = 64, 6, 200
+    flags = FORCE_FIRST | FORCE_LOCAL
+    sh, x = int_case(50 + fp8, batch=batch, n_q=n_q, n_k=n_k, heads=64, dim=128, q_pos0=n_k - n_q,
+                     lo=-2, hi=2, fp8=fp8)
+    R = batch * n_q
+    rows = np.arange(R)
+    qr, wr = x["q"].reshape(R, 64, 128), x["w"].reshape(R, 64)
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], x["k_scale"], block, m_scored, flags, topk,
+                                      rows)
+    q, w, k, ks = gpu_inputs(x)
+    idx, vals, blk = tks.hisa_topk(tks.Shape(**sh), q, w, k, ks, block, m_scored, flags, topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                      "generic block paths")
+
+
 def test_fp8_every_code_decodes_exactly():
     """One-hot keys: key c holds e4m3fn code c at dim 0, so its score is
     max(0, q0 * value(c)); compared with torch's e4m3fn decode."""
