@@ -311,6 +311,31 @@ def test_scheduled_refine_block_sizes_exact(block, m_scored, n_k, q_chunk):
                       "scheduled refine B=%d" % block)
 
 
+@pytest.mark.parametrize("ratio,q_pos0", [(4, -6), (3, 5)])
+def test_scheduled_refine_compressed_causality_exact(ratio, q_pos0):
+    """Prefill refinement through the plans with compressed causality: a
+    query sees (q_pos0 + t) / ratio + 1 keys, so neighbouring queries of a
+    group see the same or almost the same keys, and with q_pos0 < 0 the
+    first queries see none (padding rows inside a group).  Blocks and
+    tokens must equal the oracle's."""
+    say("scheduled refine, causal ratio %d, q_pos0 %d" % (ratio, q_pos0))
+    batch, n_q, n_k, heads, block, m_scored, topk = 2, 600, 2000, 64, 64, 6, 150
+    flags = FORCE_FIRST | FORCE_LOCAL
+    sh, x = int_case(60 + ratio, batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=128, q_pos0=q_pos0,
+                     ratio=ratio, lo=-2, hi=2)
+    R = batch * n_q
+    rows = np.arange(R)
+    qr, wr = x["q"].reshape(R, heads, 128), x["w"].reshape(R, heads)
+    blk_o, idx_o, val_o = oracle.hisa(sh, qr, wr, x["k"], None, block, m_scored, flags, topk, rows)
+    S = tks.Shape(**sh)
+    q, w, k, ks = gpu_inputs(x)
+    idx, vals, blk = tks.hisa_topk(S, q, w, k, ks, block, m_scored, flags, topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(blk).reshape(R, -1), blk_o)
+    assert_topk_exact(host(idx).reshape(R, -1), host(vals).reshape(R, -1), idx_o, val_o,
+                      "scheduled refine, compressed causality")
+
+
 def test_refine_plans_made_chunk_by_chunk_exact():
     """Refinement plans too large to make for every group at once (here
     4096 groups x 1024 positions) are made chunk by chunk; with 1000-row
