@@ -44,6 +44,12 @@
  *     non-OK status leaves outputs untouched.  tks_last_error() then gives
  *     a thread-local message.  Device faults surface at the caller's next
  *     synchronisation.  No C++ exception crosses this interface.
+ *   - Debugging: with the environment variable TKS_DEBUG_SYNC=1 (read once
+ *     per process), every launch is followed by a synchronisation of its
+ *     stream and a check of the HIP error state, so an asynchronous kernel
+ *     failure is returned (TKS_EHIP) by the call that launched it.  Launches
+ *     on a stream being captured into a graph are not synchronised.  The
+ *     switch changes no result; it only serialises the host with the GPU.
  */
 #ifndef TKS_H
 #define TKS_H

@@ -5,6 +5,7 @@
 // memory is allocated here.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -13,6 +14,7 @@
 #include <vector>
 
 #include "../../include/tks.h"
+
 #include "tks_launch.hpp"
 
 namespace {
@@ -29,6 +31,27 @@ int fail(int code, const char* fmt, ...) {
 
 int hip_fail(hipError_t e, const char* where) {
     return fail(TKS_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// TKS_DEBUG_SYNC=1 in the environment: every launch is followed by a
+// synchronisation of its stream (not while the stream is being captured into
+// a graph), so a failure inside a kernel is reported by the call that made
+// the launch instead of by some later HIP call.
+bool debug_sync_on() {
+    static const bool on = [] {
+        const char* v = getenv("TKS_DEBUG_SYNC");
+        return v != nullptr && v[0] == '1';
+    }();
+    return on;
+}
+
+hipError_t after_launch(hipError_t e, hipStream_t s) {
+    if (e != hipSuccess || !debug_sync_on()) return e;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(s, &cs)) != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipSuccess;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------- instrumentation
@@ -266,7 +289,7 @@ int tks_indexer_scores(const tks_shape* s, const void* q, const float* w, const 
         e = tks::launch_score(a, n_rows, s->dim, s->key_dtype == TKS_KEY_FP8_E4M3FN, false,
                               stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "score launch");
+    if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "score launch");
     return TKS_OK;
 }
 
@@ -358,7 +381,7 @@ int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void*
             Timed tm("score_flat", stream);
             e = tks::launch_score_fused(a, rows, p.n_seg, fp8k, stream);
         }
-        if (e != hipSuccess) return hip_fail(e, "fused score launch");
+        if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "fused score launch");
         tks::FusedFinishArgs f{};
         f.pool = pool;
         f.sel.rows = rm;
@@ -382,7 +405,7 @@ int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void*
             Timed tm("select_flat", stream);
             e = tks::launch_fused_finish(f, fp8k, stream);
         }
-        if (e != hipSuccess) return hip_fail(e, "fused finish launch");
+        if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "fused finish launch");
         return TKS_OK;
     }
     float* sbuf = reinterpret_cast<float*>(ws + p.off_scores);
@@ -417,7 +440,7 @@ int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void*
                 Timed tm("score_flat", stream);
                 e = tks::launch_score(a, n, s->dim, fp8, false, stream);
             }
-            if (e != hipSuccess) return hip_fail(e, "score launch");
+            if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "score launch");
 
             tks::SelectArgs sa{};
             sa.scores = sbuf;
@@ -444,7 +467,7 @@ int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void*
                 else
                     e = tks::launch_select(sa, n, stream);
             }
-            if (e != hipSuccess) return hip_fail(e, "select launch");
+            if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "select launch");
         }
     }
     return TKS_OK;
@@ -567,7 +590,7 @@ int tks_topk_scores(const float* scores, int32_t n_rows, int32_t n_cols, int64_t
         e = sp.parts > 0 ? tks::launch_select_split(sa, n_rows, sp, workspace, stream)
                          : tks::launch_select(sa, n_rows, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "select launch");
+    if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "select launch");
     return TKS_OK;
 }
 
@@ -589,7 +612,7 @@ int tks_hisa_pool_keys(const tks_shape* s, const void* k, const float* k_scale, 
         Timed tm("pool", stream);
         e = tks::launch_pool(a, s->key_dtype == TKS_KEY_FP8_E4M3FN, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "pool launch");
+    if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "pool launch");
     return TKS_OK;
 }
 
@@ -636,7 +659,7 @@ int tks_kv_append(const tks_shape* s, const void* raw, int32_t n_new, int32_t ra
         Timed tm("append", stream);
         e = tks::launch_append(a, s->dim, s->key_dtype == TKS_KEY_FP8_E4M3FN, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "append launch");
+    if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "append launch");
     return TKS_OK;
 }
 
@@ -722,7 +745,7 @@ int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, con
             Timed tm("score_pooled", stream);
             e = tks::launch_score(a, n, s->dim, false, false, stream);
         }
-        if (e != hipSuccess) return hip_fail(e, "block score launch");
+        if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "block score launch");
 
         tks::SelectArgs sa{};
         sa.scores = sbuf;
@@ -744,7 +767,7 @@ int tks_hisa_block_select(const tks_shape* s, const void* q, const float* w, con
             Timed tm("select_pooled", stream);
             e = tks::launch_select(sa, n, stream);
         }
-        if (e != hipSuccess) return hip_fail(e, "block select launch");
+        if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "block select launch");
     }
     return TKS_OK;
 }
@@ -891,7 +914,7 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
                 e = tks::launch_score(a, n, s->dim, fp8, true, stream);
             }
         }
-        if (e != hipSuccess) return hip_fail(e, "refine score launch");
+        if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "refine score launch");
 
         tks::SelectArgs sa{};
         sa.scores = sbuf;
@@ -912,7 +935,7 @@ int tks_hisa_refine_topk(const tks_shape* s, const void* q, const float* w, cons
             Timed tm("select_refine", stream);
             e = tks::launch_select(sa, n, stream);
         }
-        if (e != hipSuccess) return hip_fail(e, "refine select launch");
+        if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "refine select launch");
     }
     return TKS_OK;
 }
@@ -937,7 +960,7 @@ int tks_gather_selected(const void* kv, int32_t batch, int32_t n_kv, int32_t row
         Timed tm("gather", stream);
         e = tks::launch_gather(a, rows, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "gather launch");
     return TKS_OK;
 }
 
@@ -991,7 +1014,7 @@ int tks_sparse_attention(const void* q, const void* k, const void* v, int32_t ba
         Timed tm("attend", stream);
         e = tks::launch_attend(a, rows, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if ((e = after_launch(e, stream)) != hipSuccess) return hip_fail(e, "attention launch");
     return TKS_OK;
 }
 
