@@ -641,6 +641,44 @@ def test_hisa_ragged_cache_exact():
                           "ragged hisa B=%d" % block)
 
 
+@pytest.mark.parametrize("nb,n_q,q_pos0,heads,dim", [
+    (300, 40, None, 4, 32), (700, 601, -40, 4, 32), (1500, 37, None, 4, 32), (2600, 30, None, 4, 32),
+    (64, 9, -3, 4, 32),
+    # D = 128, fewer than 8 rows per sequence (decode-like)
+    (512, 1, None, 64, 128), (1000, 5, None, 20, 128), (2048, 3, None, 64, 128), (40, 7, 28, 64, 128),
+    (2049, 2, None, 64, 128)])
+def test_block_select_rows_exact(nb, n_q, q_pos0, heads, dim):
+    """Block selection straight from integer pooled keys in [-2, 2] (block
+    scores are integers, so nearly every kept set ends inside a tie): rows
+    of up to 512, 1024 and 2048 blocks (a wave per row) and longer rows (the
+    workgroup route), with D = 32 and with D = 128 at decode-like row counts;
+    queries that see no block, a ragged cache tail, m from 0 to more than a
+    row can keep, every force flag combination."""
+    block, batch = 32, 2
+    n_k = nb * block + 17
+    q_pos0 = n_k - n_q if q_pos0 is None else q_pos0
+    say("block select nb=%d rows=%d q_pos0=%d heads=%d dim=%d" % (nb, batch * n_q, q_pos0, heads, dim))
+    rng = np.random.default_rng(nb + n_q)
+    sh = dict(batch=batch, n_q=n_q, n_k=n_k, heads=heads, dim=dim, q_pos0=q_pos0, causal_ratio=1,
+              key_dtype=0)
+    R = batch * n_q
+    q = fp32_to_bf16_bits(rng.integers(-2, 3, (R, heads, dim)).astype(np.float32))
+    w = rng.integers(-2, 3, (R, heads)).astype(np.float32)
+    pooled = fp32_to_bf16_bits(rng.integers(-2, 3, (batch, nb, dim)).astype(np.float32))
+    S = tks.Shape(**sh)
+    qd, wd, pd = dev(q.reshape(batch, n_q, heads, dim)), dev(w.reshape(batch, n_q, heads)), dev(pooled)
+    for m, flags in ((0, FORCE_LOCAL), (5, FORCE_FIRST | FORCE_LOCAL), (62, FORCE_FIRST),
+                     (200, 0), (nb + 3, FORCE_FIRST | FORCE_LOCAL)):
+        m = min(m, 510)  # m_total at most 512
+        blk_o, bv_o = oracle.block_select(sh, q, w, pooled, block, m, flags, np.arange(R))
+        blk, bv = tks.hisa_block_select(S, qd, wd, pd, block, m, flags)
+        torch.cuda.synchronize()
+        got_b = host(blk).reshape(R, -1)
+        got_v = host(bv).reshape(R, -1).astype(np.float64)
+        np.testing.assert_array_equal(got_b, blk_o, err_msg="blocks m=%d flags=%d" % (m, flags))
+        np.testing.assert_array_equal(got_v, bv_o, err_msg="values m=%d flags=%d" % (m, flags))
+
+
 def test_small_float_flat_within_tolerance():
     say("float flat L=2048 H=64 D=128 k=512")
     cfg = scaled(CONFIGS[2], n_q=2048, n_k=2048, topk=512)
