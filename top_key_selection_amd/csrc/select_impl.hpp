@@ -1068,7 +1068,8 @@ __device__ __forceinline__ int32_t select_hist(const SelectArgs& a, const RowCtx
             if (p) L.u[kMaxK + pos] = composite(key, idx);
         };
         visit_prior<NT>(a, r, cp);
-        visit_columns<VEC, NT>(a, r, r.lo, r.hi, cp);
+        // (the columns with batched appends: one atomic per wave and group)
+        collect_ge<VEC, NT>(a, r, r.lo, r.hi, (uint32_t)bstar << kBinShift, &L.cnt[1], &L.u[kMaxK], kCap);
         __syncthreads();
         return pool_best<NT>(L, above + inbin, K, sorted);
     }
