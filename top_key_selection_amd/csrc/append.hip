@@ -27,7 +27,8 @@
 // A call that stays inside one block per sequence (a decode append) takes a
 // workgroup per sequence instead: all its threads copy the block's earlier
 // compressed keys to LDS at once (one memory round trip instead of one per
-// few keys), then the D/8 owner threads sum them from LDS in key order.
+// few keys), then one thread per dimension sums them from LDS in key order
+// and hands the sums to the D/8 owner threads.
 #include "tks_launch.hpp"
 
 namespace tks {
@@ -111,40 +112,62 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         constexpr int KB = FP8 ? D : 2 * D;  // bytes per cached key
         __shared__ __align__(16) uint8_t s_k[STAGE ? kStageMax * KB : 16];
         __shared__ float s_s[STAGE ? kStageMax : 1];
+        __shared__ double s_sum[STAGE ? D : 1];
         const int32_t n_back = gs - J * a.span;  // < block size <= 256
         const uint8_t* src = static_cast<const uint8_t*>(a.k) + (kbase + J * a.span) * KB;
-        for (int o = threadIdx.x * 16; o < n_back * KB; o += kThreads * 16)
-            *reinterpret_cast<u32x4*>(s_k + o) = *reinterpret_cast<const u32x4*>(src + o);
+        // four 16-byte loads per thread in flight before their stores
+        const int32_t nb = n_back * KB;
+        for (int32_t o0 = 0; o0 < nb; o0 += 4 * kThreads * 16) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int32_t o = o0 + (u * kThreads + (int)threadIdx.x) * 16;
+                if (o < nb) v[u] = *reinterpret_cast<const u32x4*>(src + o);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int32_t o = o0 + (u * kThreads + (int)threadIdx.x) * 16;
+                if (o < nb) *reinterpret_cast<u32x4*>(s_k + o) = v[u];
+            }
+        }
         if (FP8)
             for (int i = threadIdx.x; i < n_back; i += kThreads) s_s[i] = a.k_scale[kbase + J * a.span + i];
         __syncthreads();
-        if (piece >= TPG) return;
-        // eight rows' LDS reads issued before their sums (the sums stay in
-        // key order)
-        constexpr int U = 8;
-        for (int32_t i0 = 0; i0 < n_back; i0 += U) {
-            if constexpr (FP8) {
-                u32x2 c[U];
+        // one thread per dimension sums the earlier keys in key order (the
+        // same operations, in the same order, as the owner threads' sums)
+        if (threadIdx.x < D) {
+            const int d = threadIdx.x;
+            double acc = 0.0;
+            constexpr int U = 8;
+            for (int32_t i0 = 0; i0 < n_back; i0 += U) {
+                float x[U];
                 float sc[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int32_t i = min(i0 + u, n_back - 1);
-                    c[u] = *reinterpret_cast<const u32x2*>(s_k + i * KB + 8 * piece);
-                    sc[u] = s_s[i];
+                    if constexpr (FP8) {
+                        x[u] = __builtin_amdgcn_cvt_f32_fp8((int)s_k[i * KB + d], 0);
+                        sc[u] = s_s[i];
+                    } else {
+                        x[u] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(s_k)[i * D + d] << 16);
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (i0 + u < n_back) add_fp8x8(pacc, c[u][0], c[u][1], sc[u]);
-            } else {
-                u32x4 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[u] = *reinterpret_cast<const u32x4*>(s_k + min(i0 + u, n_back - 1) * KB + 16 * piece);
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (i0 + u < n_back) add_bf16x8(pacc, v[u]);
+                for (int u = 0; u < U; ++u) {
+                    if (i0 + u < n_back) {
+                        if constexpr (FP8)
+                            acc = fma((double)sc[u], (double)x[u], acc);
+                        else
+                            acc += (double)x[u];
+                    }
+                }
             }
+            s_sum[d] = acc;
         }
+        __syncthreads();
+        if (piece >= TPG) return;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pacc[e] = s_sum[8 * piece + e];
     } else if (STAGE && piece >= TPG) {
         return;
     } else if (pool) {
