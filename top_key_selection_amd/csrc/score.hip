@@ -451,7 +451,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     uint32_t f_lo = 0xFFFFFFFFu, f_hi = 0u;  // fused mode: range of this lane's valid keys
     __shared__ float s_w[MB * 32];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // (uniform: scalar addressing)
     const int m = lane & 31;
     const int hf = lane >> 5;
 
@@ -505,8 +505,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // all LDS banks.  Other dims copy each lane's own half row.
     constexpr bool ROT = D == 128;
     const int rr = lane >> 3, qq = lane & 7;
+    // byte offset of this lane's copy c from the sub-block's first key row
+    uint32_t loff[RG::CH];
+#pragma unroll
+    for (int c = 0; c < RG::CH; ++c) {
+        if constexpr (ROT)
+            loff[c] = (uint32_t)((8 * c + rr) * D + ((qq - rr - c) & 7) * 16);
+        else
+            loff[c] = (uint32_t)(m * D + hf * (D / 2) + c * 16);
+    }
     auto fetch = [&](int32_t u) {
         uint8_t* st = wring + (u % RG::R) * RG::STAGE;
+        // a sub-block whose 32 slots all hold visible keys is one run of key
+        // rows (a block holds whole sub-blocks): a uniform base and each
+        // lane's fixed offset, with no per-key checks (the same copies)
+#if defined(__HIP_DEVICE_COMPILE__)  // (device code only; the host pass skips it)
+        const int32_t s0 = first + u * SB;
+        int32_t kb0 = 0;
+        bool whole;
+        if constexpr (BLOCKS) {
+            const int32_t b = s0 + 32 <= limit ? __builtin_amdgcn_readfirstlane(s_blk[s0 >> a.block_shift]) : -1;
+            kb0 = (b << a.block_shift) + (s0 & bmask);
+            whole = b >= 0 && kb0 + 32 <= n_tok;
+        } else {
+            kb0 = a.col_key0 + s0;
+            whole = s0 + 32 <= limit;
+        }
+        if (whole) {
+            const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.k) + (kseq + kb0) * D;
+#pragma unroll
+            for (int c = 0; c < RG::CH; ++c) {
+                if constexpr (ROT)
+                    __builtin_amdgcn_global_load_lds(sb + loff[c], st + c * 1024, 16, 0, 2);
+                else
+                    __builtin_amdgcn_global_load_lds(sb + loff[c], st + c * 1024, 16, 0, 0);
+            }
+            __builtin_amdgcn_global_load_lds(a.k_scale + kseq + kb0 + m, st + RG::CH * 1024, 4, 0, 0);
+            return;
+        }
+#endif
         if constexpr (ROT) {
 #pragma unroll
             for (int c = 0; c < RG::CH; ++c) {
