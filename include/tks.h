@@ -119,8 +119,9 @@ int tks_indexer_scores(const tks_shape* shape, const void* q, const float* w, co
  * automatic, scoring and selection are fused instead (StreamIndex
  * abstract; the threshold-based Indexer-TopK abstract on the same page:
  * write back only the promising candidates and stay exact): each
- * 4096-key segment keeps its best candidates above a threshold of its
- * own, a finish pass selects the row's top-k from them and proves the
+ * 4096-key segment (with fp8 keys, each quarter of it that one wave
+ * scored) keeps its best candidates above a threshold of its own, a
+ * finish pass selects the row's top-k from them and proves the
  * result exact (its k-th best is at least every segment's threshold),
  * and a row that fails the proof (heavily tied or clustered scores) is
  * rescored and selected exactly.  The workspace then holds at most 4096

@@ -177,7 +177,8 @@ struct FlatPlan {
     int64_t score_stride;
     tks::SelectSplit split;  // few long rows over every CU (single tile only)
     size_t off_scores, off_run_val, off_run_idx, off_split;
-    int32_t n_seg, r_cap;    // fused
+    int32_t n_seg, r_cap;    // fused: key segments of kFusedSeg, survivors per pool segment
+    int32_t pool_split;      // fused: pool segments per key segment
     size_t off_cand, off_count, off_tau, off_failed, off_arena;
     size_t bytes;
 };
@@ -191,14 +192,20 @@ FlatPlan plan_flat(const tks_shape* s, int32_t topk, int32_t q_chunk, int32_t k_
         n_seg <= kFusedMaxSeg) {
         p.fused = true;
         p.n_seg = (int32_t)n_seg;
-        p.r_cap = std::min<int32_t>(tks::kFusedSeg, tks::kFusedPoolCap / p.n_seg);
+        // fp8 keys: every wave of a scoring workgroup filters its own keys of
+        // a segment (no workgroup barrier), while the finish can take the
+        // segments
+        p.pool_split = s->key_dtype == TKS_KEY_FP8_E4M3FN && n_seg * tks::kFusedWaves <= tks::kFusedMaxPoolSeg
+                           ? tks::kFusedWaves : 1;
+        const int64_t pseg = n_seg * p.pool_split;
+        p.r_cap = std::min<int32_t>(tks::kFusedSeg / p.pool_split, tks::kFusedPoolCap / (int32_t)pseg);
         size_t off = 0;
         p.off_cand = off;
-        off += round_up(p.rows * n_seg * p.r_cap * 8, 256);
+        off += round_up(p.rows * pseg * p.r_cap * 8, 256);
         p.off_count = off;
-        off += round_up(p.rows * n_seg * 4, 256);
+        off += round_up(p.rows * pseg * 4, 256);
         p.off_tau = off;
-        off += round_up(p.rows * n_seg * 4, 256);
+        off += round_up(p.rows * pseg * 4, 256);
         p.off_failed = off;  // failed-row list, then its counter
         off += round_up((p.rows + 1) * 4, 256);
         p.off_arena = off;
@@ -360,7 +367,8 @@ int topk_flat_run(const tks_shape* s, const void* q, const float* w, const void*
         const bool fp8k = s->key_dtype == TKS_KEY_FP8_E4M3FN;
         const tks::FusedPool pool{reinterpret_cast<uint64_t*>(ws + p.off_cand),
                                   reinterpret_cast<int32_t*>(ws + p.off_count),
-                                  reinterpret_cast<uint32_t*>(ws + p.off_tau), p.n_seg, p.r_cap};
+                                  reinterpret_cast<uint32_t*>(ws + p.off_tau), p.n_seg * p.pool_split,
+                                  p.r_cap, p.pool_split};
         const tks::RowMap rm{0, s->n_q, 0, s->n_q};
         tks::ScoreArgs a{};
         a.q = static_cast<const uint16_t*>(q);

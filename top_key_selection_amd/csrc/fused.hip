@@ -24,7 +24,7 @@ namespace tks {
 
 namespace {
 
-constexpr int kFinishMaxSeg = 256;  // segments per row (64 per lane of one wave, times 4)
+constexpr int kFinishMaxSeg = kFusedMaxPoolSeg;  // segments per row (4 per lane of one wave)
 static_assert(kFusedPoolCap == kCap, "the pool of a row fits the selection's candidate list");
 
 // Arena words per finish workgroup: a score tile and the running list
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NT) void fused_finish_kernel(FusedFinishArgs a) {
     const FusedPool& P = a.pool;
     for (int64_t y = blockIdx.x; y < a.n_rows; y += gridDim.x) {
         const int32_t n_vis = a.sel.vis.tokens(a.sel.rows.query(y));
-        const int32_t n_seg = (n_vis + kFusedSeg - 1) / kFusedSeg;
+        const int32_t n_seg = (n_vis + kFusedSeg - 1) / kFusedSeg * P.split;
         // survivor counts -> offsets, and the largest threshold (one wave)
         if (wave == 0) {
             constexpr int PER = kFinishMaxSeg / 64;

@@ -161,6 +161,115 @@ __device__ __forceinline__ void fused_filter(const uint32_t* stash, int32_t n, i
     }
 }
 
+// One wave's filter of the keys it scored in a segment, as pool segment
+// `seg` of row `row` (the waves of a workgroup then never wait for each
+// other): key[e] of each lane (0: no candidate) has key index idx_of(e);
+// lo / hi are the smallest and largest valid key the lane saw.  The rule
+// of fused_filter over 256 value bins, with wave-level reductions only;
+// hist is the wave's own 256 words of LDS (one wave's LDS instructions run
+// in program order, so no barrier orders its phases).  Survivors are
+// placed by a bitwise ballot prefix of the lanes' counts.
+template <int PER, class IDX>
+__device__ __forceinline__ void fused_filter_wave(const uint32_t (&key)[PER], IDX&& idx_of, uint32_t* hist,
+                                                  const FusedPool& P, int64_t row, int32_t seg,
+                                                  uint32_t lo, uint32_t hi) {
+    constexpr int NB = 256;
+    static_assert(PER < 32, "per-lane counts fit five bits");
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int32_t n_valid = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) n_valid += __popcll(__ballot(key[e] != 0u));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    }
+    const uint32_t kmin = lo, kmax = hi;
+    const float vmin = fz_value(kmin);
+    const float range = fz_value(kmax) - vmin;
+    float scale = range > 0.0f && range < __builtin_inff() ? (float)NB / range : 0.0f;
+    if (!(scale < __builtin_inff())) scale = 0.0f;
+    const bool filter = n_valid > P.r_cap;
+    auto bin_of = [&](uint32_t k) {
+        return (int32_t)fminf((fz_value(k) - vmin) * scale, (float)(NB - 1));
+    };
+    int32_t keep_from = 0;  // every valid key
+    if (filter) {
+        keep_from = NB;  // none, unless the bins place the boundary
+        if (scale > 0.0f) {
+#pragma unroll
+            for (int i = 0; i < NB / 64; ++i) hist[lane * (NB / 64) + i] = 0u;
+            // (the adds as inline LDS instructions: the bins never share LDS
+            // with the key ring, and a compiler atomic would first wait for
+            // every ring copy in flight)
+            const uint32_t hbase = (uint32_t)(uintptr_t)hist;
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                if (key[e]) asm volatile("ds_add_u32 %0, %1" ::"v"(hbase + 4u * (uint32_t)bin_of(key[e])), "v"(1u) : "memory");
+            // lane l holds bins NB-1-4l .. NB-4-4l (descending); the first bin
+            // at which the count from the top passes r_cap is the boundary,
+            // and the bins above it are kept
+            constexpr int BPL = NB / 64;
+            int32_t c[BPL];
+            int32_t sum = 0;
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                c[i] = (int32_t)hist[NB - 1 - (BPL * lane + i)];
+                sum += c[i];
+            }
+            int32_t inc = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int32_t v = __shfl_up(inc, o);
+                if (lane >= o) inc += v;
+            }
+            int32_t cum = inc - sum, kf = 0;
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                if (cum <= P.r_cap && cum + c[i] > P.r_cap) kf = NB - (BPL * lane + i);
+                cum += c[i];
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) kf = max(kf, __shfl_xor(kf, o));
+            if (kf > 0) keep_from = kf;
+        }
+    }
+    uint64_t* dst = P.cand + (row * P.n_seg + seg) * (int64_t)P.r_cap;
+    uint32_t kept_min = 0xFFFFFFFFu;
+    bool keep[PER];
+    int32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const uint32_t k = key[e];
+        keep[e] = k != 0u && (!filter || (keep_from < NB && scale > 0.0f && bin_of(k) >= keep_from));
+        cnt += keep[e] ? 1 : 0;
+        if (keep[e]) kept_min = min(kept_min, k);
+    }
+    int32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const uint64_t bb = __ballot((cnt >> b) & 1);
+        pre += __popcll(bb & lt) << b;
+        tot += __popcll(bb) << b;
+    }
+    int32_t pos = pre;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (keep[e]) {
+            if (pos < P.r_cap) dst[pos] = fz_composite(key[e], idx_of(e));
+            ++pos;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) kept_min = min(kept_min, (uint32_t)__shfl_xor((int)kept_min, o));
+    if (lane == 0) {
+        P.count[row * P.n_seg + seg] = min(tot, P.r_cap);
+        // every dropped key is below the smallest kept one (or above none)
+        P.tau[row * P.n_seg + seg] = !filter ? 0u : tot > 0 ? kept_min : kmax + 1u;
+    }
+}
+
 // WPR (wave per row): each wave owns one row and walks all its slots;
 // otherwise a workgroup owns one row segment and its 4 waves interleave
 // 32-slot sub-blocks.
@@ -429,10 +538,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // NW waves per workgroup, NR ring stages per wave (every launch takes four
 // waves with three stages: two workgroups per CU).
-template <int D, int MB, bool BLOCKS, bool FUSE = false, int NW = 4, int NR = 3>
+template <int D, int MB, bool BLOCKS, bool FUSE = false, int NW = 4, int NR = 3, bool WAVEF = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void score_fp8_kernel(
     ScoreArgs a, int64_t n_rows, int32_t seg_slots) {
     static_assert(!FUSE || !BLOCKS, "fused mode: contiguous row segments");
+    static_assert(!WAVEF || (FUSE && NW == kFusedWaves), "a pool segment per wave of a fused workgroup");
     constexpr int NT = NW * 64;
     constexpr int SB = NW * 32;  // slots per sub-block round of the workgroup
     using RG = Fp8Ring<D, NR>;
@@ -447,7 +557,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     constexpr int QN = FUSE && MB * 32 * QS < 2 * kFusedSeg ? 2 * kFusedSeg : MB * 32 * QS;
     __shared__ __align__(16) uint16_t s_q[QN];
     uint32_t* stash = reinterpret_cast<uint32_t*>(s_q);
-    __shared__ uint32_t s_fscr[FUSE ? NT + 32 : 1];
+    // filter scratch: the workgroup's (kFilterScratch words), or 256 bins per
+    // wave when every wave filters its own keys (WAVEF)
+    __shared__ uint32_t s_fscr[!FUSE ? 1 : WAVEF ? NW * 256 : NT + 32];
     uint32_t f_lo = 0xFFFFFFFFu, f_hi = 0u;  // fused mode: range of this lane's valid keys
     __shared__ float s_w[MB * 32];
     const int lane = threadIdx.x & 63;
@@ -610,8 +722,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
         }
     };
-    // ReLU * w head reduction and store of sub-block u
-    auto epilogue = [&](int32_t u, const f32x16* acc, float scale) {
+    // ReLU * w head reduction and store of sub-block u (WAVEF: returns the
+    // score key of slot first + u * SB + m, 0 when not visible)
+    auto epilogue = [&](int32_t u, const f32x16* acc, float scale) -> uint32_t {
         float sc = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -631,11 +744,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 f_lo = min(f_lo, key);
                 f_hi = max(f_hi, key);
             }
-        } else if (hf == 0 && slot < slot_end) {
-            if (valid)
-                a.out[y * a.out_stride + slot] = sc;
-            else if (a.write_masked)
-                a.out[y * a.out_stride + slot] = -__builtin_inff();
+            return key;
+        } else {
+            if (hf == 0 && slot < slot_end) {
+                if (valid)
+                    a.out[y * a.out_stride + slot] = sc;
+                else if (a.write_masked)
+                    a.out[y * a.out_stride + slot] = -__builtin_inff();
+            }
+            return 0u;
         }
     };
 
@@ -708,12 +825,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 // with them, so a later part starts with nothing in flight
                 // (its first stages have been landing during the filter)
                 wait_vmcnt<0>();
-                __syncthreads();  // (and the filter has read the stash)
+                if constexpr (!WAVEF) __syncthreads();  // (and the filter has read the stash)
             }
-            run(p * kPart, min(nsub, (p + 1) * kPart));
-            __syncthreads();
-            fused_filter<NT>(stash, min(min(slot_end, work_end) - h, kFusedSeg), min(limit - h, kFusedSeg), a.col_key0 + h,
-                             s_fscr, a.fuse, y, (int32_t)blockIdx.y * parts + p, f_lo, f_hi);
+            if constexpr (WAVEF) {
+                // this wave's keys of the part, read back from the stash,
+                // where only this wave wrote them (its own LDS writes, in
+                // program order: no barrier): lane (m, hf) takes sub-blocks
+                // u0 + 2e + hf; sub-blocks the wave did not reach hold none
+                constexpr int PER = kPart / 2;
+                const int32_t u0 = p * kPart, u1 = min(nsub, (p + 1) * kPart);
+                run(u0, u1);
+                uint32_t key[PER];
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    key[e] = u0 + 2 * e + hf < u1 ? stash[wave * 32 + (2 * e + hf) * SB + m] : 0u;
+                const int32_t i0 = a.col_key0 + first + (u0 + hf) * SB + m;
+                fused_filter_wave<PER>(key, [&](int e) { return i0 + e * (2 * SB); }, s_fscr + wave * 256,
+                                       a.fuse, y, ((int32_t)blockIdx.y * parts + p) * NW + wave, f_lo, f_hi);
+            } else {
+                run(p * kPart, min(nsub, (p + 1) * kPart));
+                __syncthreads();
+                fused_filter<NT>(stash, min(min(slot_end, work_end) - h, kFusedSeg), min(limit - h, kFusedSeg),
+                                 a.col_key0 + h, s_fscr, a.fuse, y, (int32_t)blockIdx.y * parts + p, f_lo, f_hi);
+            }
         }
         wait_vmcnt<0>();
     }
@@ -1765,10 +1899,18 @@ hipError_t launch_score_fused(const ScoreArgs& a, int64_t n_rows, int32_t n_seg,
         // (Eight-wave workgroups with four ring stages, one per CU, measured
         // slower: every part boundary stalls the CU's only workgroup.)
         const int32_t parts = n_rows * ((n_seg + 1) / 2) >= 512 ? 2 : 1;
-        hipLaunchKernelGGL((score_fp8_kernel<128, 2, false, true, 4, 3>),
-                           dim3((unsigned)n_rows, (unsigned)((n_seg + parts - 1) / parts)), dim3(256), 0,
-                           stream, a, n_rows, (int32_t)(parts * kFusedSeg));
+        const dim3 grid((unsigned)n_rows, (unsigned)((n_seg + parts - 1) / parts));
+        // (a pool split per wave: every wave filters its own keys)
+        if (a.fuse.split == kFusedWaves)
+            hipLaunchKernelGGL((score_fp8_kernel<128, 2, false, true, 4, 3, true>), grid, dim3(256), 0, stream, a,
+                               n_rows, (int32_t)(parts * kFusedSeg));
+        else if (a.fuse.split == 1)
+            hipLaunchKernelGGL((score_fp8_kernel<128, 2, false, true, 4, 3>), grid, dim3(256), 0, stream, a,
+                               n_rows, (int32_t)(parts * kFusedSeg));
+        else
+            return hipErrorInvalidValue;
     } else {
+        if (a.fuse.split != 1) return hipErrorInvalidValue;  // (one filter per workgroup)
         hipLaunchKernelGGL((score_kernel<128, 2, false, false, false, true>),
                            dim3((unsigned)n_rows, (unsigned)n_seg), dim3(256), 0, stream, a, n_rows,
                            (int32_t)kFusedSeg);

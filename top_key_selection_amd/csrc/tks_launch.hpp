@@ -14,16 +14,23 @@ namespace tks {
 // r_cap: every candidate whose score key is at least a threshold T of its
 // own) and writes them, with T, to the row's survivor pool.  Every dropped
 // candidate of the segment has a score key below T (T = 0: none dropped).
+// With split = kFusedWaves (fp8 keys) every wave of the workgroup does this
+// for the keys it scored, as a pool segment of its own, so the waves never
+// wait for each other.
 // The finish (fused.hip) selects the row's top-k from the pool; the result
 // is exact when its k-th best survivor's key is at least every segment's T.
 constexpr int kFusedSeg = 4096;
 constexpr int kFusedPoolCap = 4096;  // survivors of one row, all segments together
+constexpr int kFusedMaxPoolSeg = 256;  // pool segments of one row the finish takes
+constexpr int kFusedWaves = 4;       // waves of an fp8 scoring workgroup
 struct FusedPool {
     uint64_t* cand;    // [rows, n_seg, r_cap] composites (score key << 32 | ~index)
     int32_t* count;    // [rows, n_seg]
     uint32_t* tau;     // [rows, n_seg]
     int32_t n_seg;     // segments per row in the pool's layout
     int32_t r_cap;     // survivors per segment at most
+    int32_t split;     // pool segments per kFusedSeg keys: 1, or one per wave
+                       // of the scoring workgroup (each filtered on its own)
 };
 
 // Refinement schedule (score.hip): for each group of kSchedRows consecutive
