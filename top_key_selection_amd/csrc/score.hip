@@ -806,11 +806,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         // drain the copies still in flight before the wave's LDS is released
         wait_vmcnt<0>();
     } else {
-        // fused mode: the segment is parts of kFusedSeg keys (one pool
-        // segment each; sub-blocks [p * kPart, (p + 1) * kPart) of every
-        // wave hold part p).  A part is filtered while the ring copies of
-        // the next part's first stages are in flight; the filter scratch is
-        // its own LDS.
+        // fused mode: the segment is parts of kFusedSeg keys (sub-blocks
+        // [p * kPart, (p + 1) * kPart) of every wave hold part p), each one
+        // pool segment, or with WAVEF one pool segment per wave.  A part is
+        // filtered while the ring copies of the next part's first stages
+        // are in flight; the filter scratch is its own LDS.
         constexpr int32_t kPart = kFusedSeg / SB;
         static_assert(kPart * SB == kFusedSeg, "whole sub-block rounds per part");
         const int32_t parts = seg_slots / kFusedSeg;
