@@ -1,6 +1,6 @@
 """GPU parity of the fused flat form (one query per sequence, dim 128): the
-scoring pass keeps each 4096-key segment's best candidates above a
-threshold of its own, the finish selects the row's top-k from them and
+scoring pass keeps each 4096-key segment's best candidates (with fp8 keys,
+each wave's share of the segment) above a threshold of its own, the finish selects the row's top-k from them and
 proves it exact, and rows that fail the proof are rescored and selected
 exactly.  Integer inputs give exact fp32 scores, so indices and values must
 equal the oracle's bit for bit whichever path a row takes; the tests force
@@ -76,6 +76,21 @@ def test_fused_decode_integer_exact(fp8, n_k, topk):
     gi, gv, redone = run_fused(sh, x, topk)
     print("rows redone by rescoring: %d of %d" % (redone, sh["batch"]), flush=True)
     assert_topk_exact(gi, gv, oi, ov, "fused decode")
+
+
+@pytest.mark.parametrize("n_k", [262144, 266241])
+def test_fused_fp8_long_rows_take_both_filter_forms_exactly(n_k):
+    """With fp8 keys every wave of a scoring workgroup filters its own keys as
+    a pool segment (four per 4096-key segment) while the finish can take the
+    segments (at most 256: rows of up to 262144 keys); longer rows keep one
+    filter per 4096-key segment across the workgroup.  Both forms exact on
+    integer inputs."""
+    say("fused fp8 long rows n_k=%d" % n_k)
+    sh, x = decode_case(31 + n_k % 7, 2, n_k, heads=4, fp8=True)
+    oi, ov = oracle_rows(sh, x, 2048)
+    gi, gv, redone = run_fused(sh, x, 2048)
+    print("rows redone by rescoring: %d of %d" % (redone, sh["batch"]), flush=True)
+    assert_topk_exact(gi, gv, oi, ov, "fused fp8 n_k=%d" % n_k)
 
 
 @pytest.mark.parametrize("q_pos0,ratio", [(6500, 1), (40000, 4), (-3, 4), (0, 1)])
